@@ -1,0 +1,149 @@
+/*
+ * mhgemm.h -- C ABI of the tiled dense matrix multiply for the AMD MI355X (gfx950).
+ *
+ * The operation (the element formula of the product in "CUDA tile", 2.1, and the
+ * GEMM example of the roofline section of "Tiling 策略与内存层次优化"):
+ *
+ *     C[i][j] = sum over k in [0, K) of A(i,k) * B(k,j),   0 <= i < M, 0 <= j < N,
+ *
+ * with products of the input element type accumulated in fp32 and the sum written
+ * once to C in the output element type (fp32 as is; fp16 / bf16 rounded to nearest,
+ * ties to even).  C is overwritten: there is no alpha / beta scaling.
+ *
+ * Storage (elements, not bytes; every leading dimension counts elements):
+ *     A row-major:    A(i,k) = A[i*lda + k]      requires lda >= K
+ *     A column-major: A(i,k) = A[k*lda + i]      requires lda >= M
+ *     B row-major:    B(k,j) = B[k*ldb + j]      requires ldb >= N
+ *     B column-major: B(k,j) = B[j*ldb + k]      requires ldb >= K   ("K-contiguous")
+ *     C row-major:    C(i,j) = C[i*ldc + j]      requires ldc >= N
+ * A leading dimension is only checked against its extent when both extents of the
+ * operand are non-zero.
+ *
+ * Work split (the three tiling levels of "Tiling 策略与内存层次优化", multi-level
+ * tiling section): each workgroup owns one BM x BN tile of C, walks K in BK-deep
+ * slabs staged through LDS, and each wave accumulates a register tile with matrix
+ * (MFMA) instructions for fp16 / bf16 inputs or fused multiply-adds for fp32 inputs.
+ * The launch grid is ceil(M/BM) x ceil(N/BN) workgroups (scheduling stage of the
+ * same page), times the split-K factor where the plan splits K across workgroups.
+ *
+ * Ownership: A, B and C are device pointers owned by the caller.  A plan is an
+ * immutable host object; it may own a device workspace (split-K partial sums), which
+ * gemm_destroy frees.  Calls that run the same plan on different streams
+ * concurrently must use distinct C; a plan with a workspace (see
+ * gemm_plan_describe, field 15) must not run concurrently with itself.  C must not
+ * alias A or B.
+ *
+ * Errors: gemm_plan and gemm_plan_config return NULL on invalid arguments and set a
+ * thread-local message readable with gemm_last_error.  gemm_run returns GEMM_OK or
+ * a negative GEMM_ERR_* code.  gemm_run is asynchronous on the given stream; a
+ * device-side fault surfaces at the caller's next synchronisation of that stream.
+ */
+#ifndef MHGEMM_H
+#define MHGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct gemm_plan_s *gemm_plan_t;
+
+/* <input type>_<output type>; accumulation is always fp32. */
+enum gemm_dtype {
+    GEMM_F32_F32 = 0,
+    GEMM_F16_F16 = 1,
+    GEMM_F16_F32 = 2,
+    GEMM_BF16_BF16 = 3,
+    GEMM_BF16_F32 = 4
+};
+
+/* layout = (A flag) | (B flag).  C is always row-major. */
+enum gemm_layout {
+    GEMM_A_ROW = 0,
+    GEMM_A_COL = 1,
+    GEMM_B_ROW = 0,
+    GEMM_B_COL = 2
+};
+
+enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = -1,
+    GEMM_ERR_UNSUPPORTED = -2,
+    GEMM_ERR_HIP = -3,
+    GEMM_ERR_ALLOC = -4
+};
+
+/* Kernel families a plan can select (field 0 of gemm_plan_describe). */
+enum gemm_kind {
+    GEMM_KIND_NONE = 0,   /* M == 0, N == 0 or K == 0: no product to compute */
+    GEMM_KIND_FMA = 1,    /* fp32: LDS-staged slabs, per-lane TM x TN register tile of FMAs */
+    GEMM_KIND_MFMA = 2,   /* fp16 / bf16: LDS-staged slabs, per-wave MFMA register tiles */
+    GEMM_KIND_SKINNY = 3  /* fp16 / bf16, M <= 16: K split across waves and workgroups */
+};
+
+/*
+ * gemm_plan -- validate a problem and choose its tile configuration and grid.
+ *
+ * Host only; queries the current HIP device's compute-unit count once, and falls
+ * back to the MI355X's 256 compute units when no device answers.  The choice
+ * follows the pages' feasibility rules ("Tiling 策略与内存层次优化", constraints 1-3:
+ * LDS bytes = (BM*BK + BK*BN) * elem * stages within the 160 KB LDS of a compute
+ * unit, registers without spills, occupancy) and scores the survivors by tile
+ * arithmetic intensity 2*BM*BN / ((BM+BN)*elem) (same page, how tiling raises
+ * intensity) and by how evenly the workgroups fill the compute units ("GPU
+ * Kernel 的 Tile、Grid、Wave 与 Launch Overhead", wave section and per-shape
+ * choices).  M, N, K >= 0; dtype a gemm_dtype; layout a gemm_layout combination.
+ * Returns NULL on invalid arguments (message via gemm_last_error).  A plan for
+ * M == 0 or N == 0 runs as a no-op; a plan for K == 0 fills C with zeros (the
+ * empty sum).
+ */
+gemm_plan_t gemm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                      int dtype, int layout);
+
+/*
+ * gemm_plan_config -- like gemm_plan, but with the tile configuration forced.
+ *
+ * cfg[0..7] = { kind (gemm_kind), BM, BN, BK, waves along M, waves along N,
+ * LDS stages, split-K factor }.  The configuration must be one of the compiled
+ * variants for this input type (gemm_plan_describe of a gemm_plan result shows
+ * valid ones) and must fit the LDS budget; otherwise NULL with a message.  For
+ * sweeps of the tile space ("Tiling 策略与内存层次优化", autotuning section) and for
+ * the pages' worked launch geometries (e.g. a 64 x 64 product as 2 x 2 tiles of
+ * 32 x 32, "CUDA tile", 2.1).
+ */
+gemm_plan_t gemm_plan_config(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                             int64_t ldc, int dtype, int layout, const int32_t cfg[8]);
+
+/*
+ * gemm_run -- enqueue C = A x B on a HIP stream (hipStream_t passed as void *;
+ * NULL is the null stream).  A, B, C: device pointers laid out as described at the
+ * top of this file.  Pointers need only element alignment: operands whose base
+ * address, leading dimension or contiguous extent is not a multiple of 16 bytes
+ * are staged with narrower loads.  NULL operands are rejected when the operand has
+ * elements to read or write.  Returns GEMM_OK, GEMM_ERR_INVALID_ARG, or
+ * GEMM_ERR_HIP when the launch itself fails.  Never synchronises.
+ */
+int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stream);
+
+/* gemm_destroy -- release a plan and its workspace.  NULL is ignored. */
+void gemm_destroy(gemm_plan_t plan);
+
+/* gemm_last_error -- message of the last failure on this thread ("" if none). */
+const char *gemm_last_error(void);
+
+/*
+ * gemm_plan_describe -- the chosen configuration, for tests and reports.
+ * out[0..15] = { kind, BM, BN, BK, waves along M, waves along N, stages, split-K,
+ *                grid x, grid y, grid z, threads per workgroup, LDS bytes per
+ *                workgroup, compute units assumed, catalogue index,
+ *                workspace bytes }.
+ * Returns GEMM_OK, or GEMM_ERR_INVALID_ARG for a NULL plan or output.
+ */
+int gemm_plan_describe(gemm_plan_t plan, int32_t out[16]);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHGEMM_H */

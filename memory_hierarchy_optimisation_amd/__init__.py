@@ -1,0 +1,127 @@
+"""Python binding of libmhgemm (include/mhgemm.h): argument marshalling only.
+
+Every step of the product runs in the HIP kernels of ``libmhgemm.so``; this module
+loads that library (raising ImportError when it has not been built: there is no
+fallback path), converts tensors to device pointers and streams to ``hipStream_t``
+handles, and turns error codes into exceptions.  PyTorch is used only for device
+memory and streams.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmhgemm.so")
+
+GEMM_F32_F32, GEMM_F16_F16, GEMM_F16_F32, GEMM_BF16_BF16, GEMM_BF16_F32 = range(5)
+GEMM_A_ROW, GEMM_A_COL, GEMM_B_ROW, GEMM_B_COL = 0, 1, 0, 2
+GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED, GEMM_ERR_HIP, GEMM_ERR_ALLOC = 0, -1, -2, -3, -4
+GEMM_KIND_NONE, GEMM_KIND_FMA, GEMM_KIND_MFMA, GEMM_KIND_SKINNY = range(4)
+
+# (input element, output element) of each gemm_dtype, and back.
+DTYPES = {
+    GEMM_F32_F32: ("f32", "f32"),
+    GEMM_F16_F16: ("f16", "f16"),
+    GEMM_F16_F32: ("f16", "f32"),
+    GEMM_BF16_BF16: ("bf16", "bf16"),
+    GEMM_BF16_F32: ("bf16", "f32"),
+}
+DTYPE_OF = {v: k for k, v in DTYPES.items()}
+
+DESCRIBE_FIELDS = ("kind", "bm", "bn", "bk", "waves_m", "waves_n", "stages", "split_k",
+                   "grid_x", "grid_y", "grid_z", "threads", "lds_bytes", "cus", "variant",
+                   "workspace_bytes")
+
+EXPORTS = ("gemm_plan", "gemm_plan_config", "gemm_run", "gemm_destroy", "gemm_last_error",
+           "gemm_plan_describe")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, code, message):
+        super().__init__(f"{message} (status {code})")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                          "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    lib.gemm_plan.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32]
+    lib.gemm_plan.restype = vp
+    lib.gemm_plan_config.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32,
+                                     ctypes.POINTER(ctypes.c_int32)]
+    lib.gemm_plan_config.restype = vp
+    lib.gemm_run.argtypes = [vp, vp, vp, vp, vp]
+    lib.gemm_run.restype = i32
+    lib.gemm_destroy.argtypes = [vp]
+    lib.gemm_destroy.restype = None
+    lib.gemm_last_error.argtypes = []
+    lib.gemm_last_error.restype = ctypes.c_char_p
+    lib.gemm_plan_describe.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
+    lib.gemm_plan_describe.restype = i32
+    return lib
+
+
+_lib = _load()
+
+
+def gemm_last_error():
+    return _lib.gemm_last_error().decode()
+
+
+def gemm_plan(M, N, K, lda, ldb, ldc, dtype, layout):
+    """Plan handle (an int) for C[M,N] = A[M,K] x B[K,N]; raises GemmError on bad input."""
+    h = _lib.gemm_plan(M, N, K, lda, ldb, ldc, dtype, layout)
+    if not h:
+        raise GemmError(GEMM_ERR_INVALID_ARG, gemm_last_error())
+    return h
+
+
+def gemm_plan_config(M, N, K, lda, ldb, ldc, dtype, layout, cfg):
+    """Plan with a forced configuration cfg = (kind, BM, BN, BK, waves_m, waves_n, stages, split_k)."""
+    arr = (ctypes.c_int32 * 8)(*[int(x) for x in cfg])
+    h = _lib.gemm_plan_config(M, N, K, lda, ldb, ldc, dtype, layout, arr)
+    if not h:
+        raise GemmError(GEMM_ERR_INVALID_ARG, gemm_last_error())
+    return h
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        if x.device.type != "cuda":
+            raise ValueError("operands must be device tensors")
+        return x.data_ptr()
+    raise TypeError(f"cannot take a device pointer from {type(x).__name__}")
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def gemm_run(plan, A, B, C, stream=None):
+    """Enqueue the planned product on ``stream`` (default: torch's current stream)."""
+    rc = _lib.gemm_run(plan, _ptr(A), _ptr(B), _ptr(C), _stream(stream))
+    if rc != GEMM_OK:
+        raise GemmError(rc, gemm_last_error())
+
+
+def gemm_destroy(plan):
+    _lib.gemm_destroy(plan)
+
+
+def gemm_plan_describe(plan):
+    out = (ctypes.c_int32 * 16)()
+    rc = _lib.gemm_plan_describe(plan, out)
+    if rc != GEMM_OK:
+        raise GemmError(rc, gemm_last_error())
+    return dict(zip(DESCRIBE_FIELDS, list(out)))

@@ -1,0 +1,157 @@
+// capi.hip -- the extern "C" boundary declared in include/mhgemm.h.
+//
+// gemm_plan validates and selects a tile configuration on the host; gemm_run checks
+// pointers, decides per operand whether 16-byte loads are legal (aligned base and
+// leading dimension), and enqueues one kernel on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "../../include/mhgemm.h"
+#include "plan.h"
+
+namespace mhg {
+hipError_t launch_fma(int launcher, const LaunchArgs &p, hipStream_t s);
+hipError_t launch_mfma(int launcher, const LaunchArgs &p, hipStream_t s);
+hipError_t launch_fill(const LaunchArgs &p, hipStream_t s);
+}  // namespace mhg
+
+struct gemm_plan_s {
+  mhg::PlanData d;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+void set_error(const std::string &msg) { g_last_error = msg; }
+
+// Compute units of the current device; the MI355X's 256 when no device answers
+// (planning is host-only and also runs where there is no GPU).
+mhg::Hardware query_hardware() {
+  mhg::Hardware hw;
+  int dev = 0;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+      hw.cus = cus;
+  }
+  (void)hipGetLastError();
+  return hw;
+}
+
+gemm_plan_t make_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                      int dtype, int layout, const int32_t *cfg) {
+  mhg::PlanData d;
+  std::string err;
+  if (!mhg::validate(M, N, K, lda, ldb, ldc, dtype, layout, &d, &err)) {
+    set_error(err);
+    return nullptr;
+  }
+  const mhg::Hardware hw = query_hardware();
+  const bool ok = cfg ? mhg::force(&d, hw, cfg, &err) : mhg::select(&d, hw, &err);
+  if (!ok) {
+    set_error(err);
+    return nullptr;
+  }
+  gemm_plan_s *plan = new (std::nothrow) gemm_plan_s;
+  if (!plan) {
+    set_error("gemm_plan: out of host memory");
+    return nullptr;
+  }
+  plan->d = d;
+  set_error("");
+  return plan;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_plan_t gemm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                      int dtype, int layout) {
+  return make_plan(M, N, K, lda, ldb, ldc, dtype, layout, nullptr);
+}
+
+gemm_plan_t gemm_plan_config(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
+                             int64_t ldc, int dtype, int layout, const int32_t cfg[8]) {
+  if (!cfg) {
+    set_error("gemm_plan_config: NULL configuration");
+    return nullptr;
+  }
+  return make_plan(M, N, K, lda, ldb, ldc, dtype, layout, cfg);
+}
+
+int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stream) {
+  if (!plan) {
+    set_error("gemm_run: NULL plan");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  const mhg::PlanData &d = plan->d;
+  if (d.M == 0 || d.N == 0) return GEMM_OK;
+  if (!C) {
+    set_error("gemm_run: NULL C");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  mhg::LaunchArgs a{};
+  a.A = A;
+  a.B = B;
+  a.C = C;
+  a.M = d.M; a.N = d.N; a.K = d.K;
+  a.lda = d.lda; a.ldb = d.ldb; a.ldc = d.ldc;
+  a.in_code = d.in_code;
+  a.out_code = d.out_code;
+  a.a_col = (d.layout & GEMM_A_COL) ? 1 : 0;
+  a.b_col = (d.layout & GEMM_B_COL) ? 1 : 0;
+  a.gm = d.gm;
+  a.gn = d.gn;
+  a.split_k = d.gz;
+  a.group_m = d.group_m;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (d.K == 0) {
+    e = mhg::launch_fill(a, s);
+  } else {
+    if (!A || !B) {
+      set_error("gemm_run: NULL A or B");
+      return GEMM_ERR_INVALID_ARG;
+    }
+    const int elems16 = 16 / mhg::elem_bytes(d.in_code);
+    a.vec_a = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && (d.lda % elems16 == 0);
+    a.vec_b = (reinterpret_cast<uintptr_t>(B) % 16 == 0) && (d.ldb % elems16 == 0);
+    int count;
+    const mhg::Variant &v = mhg::catalogue(&count)[d.variant];
+    switch (d.cfg.kind) {
+      case GEMM_KIND_FMA: e = mhg::launch_fma(v.launcher, a, s); break;
+      case GEMM_KIND_MFMA: e = mhg::launch_mfma(v.launcher, a, s); break;
+      default: e = hipErrorInvalidValue; break;
+    }
+  }
+  if (e != hipSuccess) {
+    set_error(std::string("gemm_run: launch failed: ") + hipGetErrorString(e));
+    return GEMM_ERR_HIP;
+  }
+  return GEMM_OK;
+}
+
+void gemm_destroy(gemm_plan_t plan) { delete plan; }
+
+const char *gemm_last_error(void) { return g_last_error.c_str(); }
+
+int gemm_plan_describe(gemm_plan_t plan, int32_t out[16]) {
+  if (!plan || !out) {
+    set_error("gemm_plan_describe: NULL argument");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  const mhg::PlanData &d = plan->d;
+  const int32_t v[16] = {d.cfg.kind, d.cfg.bm, d.cfg.bn, d.cfg.bk, d.cfg.waves_m, d.cfg.waves_n,
+                         d.cfg.stages, d.cfg.split_k, d.gm, d.gn, d.gz, d.threads, d.lds_bytes,
+                         d.cus, d.variant, int32_t(d.ws_bytes)};
+  std::memcpy(out, v, sizeof v);
+  return GEMM_OK;
+}
+
+}  // extern "C"

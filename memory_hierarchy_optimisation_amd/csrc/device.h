@@ -1,0 +1,76 @@
+// device.h -- gfx950 device helpers shared by the kernels: vector types, the
+// workgroup -> C-tile mapping, output conversion and the LDS transpose read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "plan.h"
+
+namespace mhg {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+#define MHG_LDS __attribute__((address_space(3)))
+
+struct HalfF16 {};
+struct HalfBF16 {};
+
+// One 16x16x32 matrix multiply-accumulate on a wave: acc += A(16x32) * B(32x16).
+// Lane l holds A row (l % 16), k = 8*(l/16) .. +7 and B column (l % 16) over the same
+// k; the accumulator holds rows 4*(l/16) .. +3 of column (l % 16).
+__device__ __forceinline__ f32x4 mfma16(HalfBF16, u32x4 a, u32x4 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(HalfF16, u32x4 a, u32x4 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+
+// LDS transpose read of four 16-bit elements.  Within each group of 16 lanes, lane t
+// receives element (t & 3) of the 8-byte rows addressed by lanes 4q + (t >> 2),
+// q = 0..3: a 4 x 16 block of a row-major tile comes back column by column.
+__device__ __forceinline__ u32x2 lds_read_tr16(const char *lds_byte_ptr) {
+  bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MHG_LDS bf16x4 *)(lds_byte_ptr));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Workgroup id -> (tile row, tile column).  Consecutive workgroup ids are dispatched
+// round-robin over the 8 XCDs, each with its own L2, so ids are first regrouped so
+// that every XCD receives a contiguous run of logical tiles; logical tiles are then
+// walked group_m rows of tiles at a time, so that the tiles in flight on one XCD
+// share A row-panels and B column-panels ("Tiling 策略与内存层次优化", L2 cache: hit
+// rate is raised only through the access pattern).
+__device__ __forceinline__ void tile_of(int bid, int gm, int gn, int group_m, int &tm, int &tn) {
+  const int nwg = gm * gn;
+  const int q = nwg >> 3, r = nwg & 7;
+  const int x = bid & 7, loc = bid >> 3;
+  const int logical = x * q + min(x, r) + loc;
+  const int per_group = group_m * gn;
+  const int g = logical / per_group;
+  const int first = g * group_m;
+  const int gsz = min(gm - first, group_m);
+  const int in = logical - g * per_group;
+  tm = first + in % gsz;
+  tn = in / gsz;
+}
+
+// fp32 -> output element, round to nearest even for the 16-bit types.
+__device__ __forceinline__ void store_out(void *C, int64_t idx, float v, int out_code) {
+  if (out_code == E_F32) {
+    reinterpret_cast<float *>(C)[idx] = v;
+  } else if (out_code == E_F16) {
+    reinterpret_cast<_Float16 *>(C)[idx] = (_Float16)v;
+  } else {
+    reinterpret_cast<__bf16 *>(C)[idx] = (__bf16)v;
+  }
+}
+
+}  // namespace mhg

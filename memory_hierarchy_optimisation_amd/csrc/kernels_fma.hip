@@ -1,0 +1,160 @@
+// kernels_fma.hip -- fp32 tiled GEMM on the vector ALUs, and the zero fill for K = 0.
+//
+// The shape is the register-tiled kernel of "CUDA tile", 2.2, written for 64-lane
+// waves: a workgroup of (BM/TM) x (BN/TN) lanes owns a BM x BN tile of C and walks K
+// in slabs of BK; every lane accumulates a TM x TN block of C in registers as an
+// outer product of a TM-vector of A and a TN-vector of B per k ("寄存器Tiling", 1.1:
+// the register level of the three tiling levels).  Slabs are double-buffered in LDS
+// (one barrier per slab).  Both tiles are stored k-major so that a lane's TM (TN)
+// operand values are contiguous in LDS and come back as 16-byte reads; each k-row
+// is padded by four floats ("CUDA tile", 4, padding against bank conflicts).
+// Out-of-range loads are zero ("CUDA tile", 4: 0 is the identity of the sum) and
+// stores are masked.
+#include "device.h"
+
+namespace mhg {
+namespace {
+
+template <int BM, int BN, int BK, int TM, int TN, bool A_COL, bool B_COL>
+__global__ void __launch_bounds__((BM / TM) * (BN / TN))
+fma_gemm(LaunchArgs p) {
+  constexpr int TX = BN / TN, TY = BM / TM, NT = TX * TY;
+  constexpr int AP = BM + 4, BP = BN + 4;
+  constexpr int A_PER = BM * BK / NT, B_PER = BK * BN / NT;
+  static_assert((BM * BK) % NT == 0 && (BK * BN) % NT == 0, "slab must divide over the lanes");
+  __shared__ __attribute__((aligned(16))) float As[2][BK][AP];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK][BP];
+
+  int tm, tn;
+  tile_of(blockIdx.x, p.gm, p.gn, p.group_m, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tx = threadIdx.x % TX, ty = threadIdx.x / TX;
+  const float *__restrict__ A = static_cast<const float *>(p.A);
+  const float *__restrict__ B = static_cast<const float *>(p.B);
+
+  // Element e of the A slab -> (r, c) = (row of the C tile, k within the slab),
+  // numbered so that consecutive lanes read consecutive addresses of the storage.
+  auto a_rc = [](int e, int &r, int &c) {
+    if (A_COL) { c = e / BM; r = e % BM; } else { r = e / BK; c = e % BK; }
+  };
+  auto b_rc = [](int e, int &r, int &c) {  // r: column of the C tile, c: k
+    if (B_COL) { r = e / BK; c = e % BK; } else { c = e / BN; r = e % BN; }
+  };
+
+  float ra[A_PER], rb[B_PER];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      int r, c;
+      a_rc(int(threadIdx.x) + i * NT, r, c);
+      const int64_t gm = m0 + r, gk = k0 + c;
+      ra[i] = (gm < p.M && gk < p.K) ? A[A_COL ? gk * p.lda + gm : gm * p.lda + gk] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+      int r, c;
+      b_rc(int(threadIdx.x) + i * NT, r, c);
+      const int64_t gn = n0 + r, gk = k0 + c;
+      rb[i] = (gn < p.N && gk < p.K) ? B[B_COL ? gn * p.ldb + gk : gk * p.ldb + gn] : 0.f;
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_PER; ++i) {
+      int r, c;
+      a_rc(int(threadIdx.x) + i * NT, r, c);
+      As[buf][c][r] = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER; ++i) {
+      int r, c;
+      b_rc(int(threadIdx.x) + i * NT, r, c);
+      Bs[buf][c][r] = rb[i];
+    }
+  };
+
+  float acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
+
+  const int KT = int((p.K + BK - 1) / BK);
+  load(0);
+  store(0);
+  __syncthreads();
+  for (int t = 0; t < KT; ++t) {
+    const int cur = t & 1;
+    const bool more = t + 1 < KT;
+    if (more) load((t + 1) * BK);
+#pragma unroll
+    for (int k = 0; k < BK; ++k) {
+      float a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = As[cur][k][ty * TM + i];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = Bs[cur][k][tx * TN + j];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+    }
+    if (more) store(cur ^ 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    const int64_t row = m0 + ty * TM + i;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int64_t col = n0 + tx * TN + j;
+      if (row < p.M && col < p.N) store_out(p.C, row * p.ldc + col, acc[i][j], p.out_code);
+    }
+  }
+}
+
+template <int BM, int BN, int BK, int TM, int TN>
+hipError_t launch_fma_tiles(const LaunchArgs &p, hipStream_t s) {
+  const dim3 grid(unsigned(p.gm) * unsigned(p.gn)), block((BM / TM) * (BN / TN));
+  if (!p.a_col && !p.b_col)
+    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, false, false>), grid, block, 0, s, p);
+  else if (!p.a_col && p.b_col)
+    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, false, true>), grid, block, 0, s, p);
+  else if (p.a_col && !p.b_col)
+    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, true, false>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, true, true>), grid, block, 0, s, p);
+  return hipGetLastError();
+}
+
+// C = 0 for K = 0 (the empty sum), any output type.
+__global__ void fill_zero(void *C, int64_t M, int64_t N, int64_t ldc, int out_code) {
+  const int64_t total = M * N;
+  for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
+       e += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t i = e / N, j = e % N;
+    store_out(C, i * ldc + j, 0.f, out_code);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fma(int launcher, const LaunchArgs &p, hipStream_t s) {
+  switch (launcher) {
+    case L_FMA_32: return launch_fma_tiles<32, 32, 32, 2, 2>(p, s);
+    case L_FMA_64: return launch_fma_tiles<64, 64, 16, 4, 4>(p, s);
+    case L_FMA_128: return launch_fma_tiles<128, 128, 16, 8, 8>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_fill(const LaunchArgs &p, hipStream_t s) {
+  const int64_t total = p.M * p.N;
+  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 4096);
+  hipLaunchKernelGGL(fill_zero, dim3(unsigned(std::max<int64_t>(blocks, 1))), dim3(256), 0, s, p.C,
+                     p.M, p.N, p.ldc, p.out_code);
+  return hipGetLastError();
+}
+
+}  // namespace mhg

@@ -1,0 +1,107 @@
+"""Helpers shared by the GPU parity tests: run the HIP path through the C ABI with
+guard bands around C, and compare against the oracle at the stated bars.
+
+Bars (stated for the product on fp32 accumulation):
+  * fp32 outputs: normwise relative error ||C - C_ref||_F / ||C_ref||_F <= 1e-5;
+  * fp16 / bf16 outputs: elementwise |C - C_ref| <= 1e-2 * (|C_ref| + 1) against the
+    unrounded binary64 C_ref;
+  * bit-exact: where every fp32 partial sum is exact (small-integer inputs), the
+    output equals C_ref rounded to nearest even by the oracle's own encoder.
+"""
+import numpy as np
+import torch
+
+import memory_hierarchy_optimisation_amd as mh
+import oracle
+import synth
+
+SENTINEL16 = 0x7E5A            # written around and beside C; must survive untouched
+SENTINEL32 = 0x7FC0DEAD
+GUARD = 256                    # elements of guard band before and after C
+
+
+def dtype_code(in_t, out_t):
+    return mh.DTYPE_OF[(in_t, out_t)]
+
+
+def _to_device(storage, offset):
+    """Copy a CPU storage tensor to the GPU, optionally starting `offset` elements
+    into a larger buffer (to misalign it); returns (buffer, view)."""
+    flat = storage.reshape(-1)
+    buf = torch.empty(max(flat.numel() + offset, 1), dtype=flat.dtype, device="cuda")
+    if flat.numel():
+        buf[offset:offset + flat.numel()].copy_(flat)
+    return buf, buf[offset:]
+
+
+def run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col=False, b_col=False, ldc=None, cfg=None,
+            offset_a=0, offset_b=0, offset_c=0):
+    """Run C = A x B on the GPU.  Returns (C values float64 [M,N], C raw storage [M,N]
+    numpy (uint16 patterns or float32), plan description)."""
+    ldc = N if ldc is None else ldc
+    layout = (mh.GEMM_A_COL if a_col else 0) | (mh.GEMM_B_COL if b_col else 0)
+    code = dtype_code(in_t, out_t)
+    _, A = _to_device(As, offset_a)
+    _, B = _to_device(Bs, offset_b)
+    n_c = M * ldc
+    total = GUARD + offset_c + n_c + GUARD
+    if out_t == "f32":
+        cbuf = torch.full((total,), SENTINEL32, dtype=torch.int32, device="cuda")
+    else:
+        cbuf = torch.full((total,), SENTINEL16, dtype=torch.int16, device="cuda")
+    C = cbuf[GUARD + offset_c:]
+    if cfg is None:
+        plan = mh.gemm_plan(M, N, K, lda, ldb, ldc, code, layout)
+    else:
+        plan = mh.gemm_plan_config(M, N, K, lda, ldb, ldc, code, layout, cfg)
+    try:
+        desc = mh.gemm_plan_describe(plan)
+        mh.gemm_run(plan, A, B, C)
+        torch.cuda.synchronize()
+    finally:
+        mh.gemm_destroy(plan)
+    host = cbuf.cpu().numpy()
+    sent = SENTINEL32 if out_t == "f32" else SENTINEL16
+    raw_sent = np.array([sent], dtype=host.dtype)[0]
+    assert np.all(host[:GUARD + offset_c] == raw_sent), "write before C"
+    assert np.all(host[GUARD + offset_c + n_c:] == raw_sent), "write after C"
+    body = host[GUARD + offset_c:GUARD + offset_c + n_c].reshape(M, ldc) if M else host[:0].reshape(0, ldc)
+    assert np.all(body[:, N:] == raw_sent), "write into the padding columns of C"
+    body = np.ascontiguousarray(body[:, :N])
+    if out_t == "f32":
+        raw = body.view(np.float32)
+        vals = raw.astype(np.float64)
+    else:
+        raw = body.view(np.uint16)
+        vals = oracle.decode(raw, out_t)
+    return vals, raw, desc
+
+
+def oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col=False, b_col=False, rows=None):
+    return oracle.gemm(M, N, K, synth.to_storage_numpy(As), lda, synth.to_storage_numpy(Bs), ldb,
+                       in_t, a_col=a_col, b_col=b_col, rows=rows)
+
+
+def check_tolerance(C, Cref, out_t, what=""):
+    if out_t == "f32":
+        num = float(np.linalg.norm(C - Cref))
+        den = float(np.linalg.norm(Cref))
+        assert np.all(np.isfinite(C)), f"non-finite output {what}"
+        assert num <= 1e-5 * den or (den == 0.0 and num == 0.0), \
+            f"normwise relative error {num / max(den, 1e-300):.3e} > 1e-5 {what}"
+    else:
+        err = np.abs(C - Cref)
+        bound = 1e-2 * (np.abs(Cref) + 1.0)
+        bad = ~(err <= bound)
+        assert not bad.any(), (f"{int(bad.sum())} elements out of tolerance {what}; first at "
+                               f"{np.argwhere(bad)[0].tolist()}: got {C[bad][0]} want {Cref[bad][0]}")
+
+
+def check_exact(raw, Cref, out_t, what=""):
+    if out_t == "f32":
+        want = Cref.astype(np.float32)
+        assert np.array_equal(want.astype(np.float64), Cref), "reference not exact in fp32"
+        bad = raw != want
+    else:
+        bad = raw != oracle.encode(Cref, out_t)
+    assert not bad.any(), f"{int(bad.sum())} elements differ bitwise {what}; first at {np.argwhere(bad)[0].tolist()}"

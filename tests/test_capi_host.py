@@ -1,0 +1,146 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and exports every
+function the header declares, arguments are validated, and the planner's choices
+follow the pages' rules (LDS budget, grid geometry, per-shape regimes).  No kernel
+is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import memory_hierarchy_optimisation_amd as mh
+from oracle import formulas as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mhgemm.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("gemm_plan", "gemm_run", "gemm_destroy", "gemm_last_error",
+                     "gemm_plan_describe", "gemm_plan_config"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(mh.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert set(_declared_functions()) == set(mh.EXPORTS)
+
+
+def _plan(M, N, K, dtype, layout=0, lda=None, ldb=None, ldc=None, cfg=None):
+    a_col, b_col = layout & 1, layout & 2
+    lda = (M if a_col else K) if lda is None else lda
+    ldb = (K if b_col else N) if ldb is None else ldb
+    ldc = N if ldc is None else ldc
+    p = mh.gemm_plan(M, N, K, lda, ldb, ldc, dtype, layout) if cfg is None else \
+        mh.gemm_plan_config(M, N, K, lda, ldb, ldc, dtype, layout, cfg)
+    try:
+        return mh.gemm_plan_describe(p)
+    finally:
+        mh.gemm_destroy(p)
+
+
+@pytest.mark.parametrize("args,msg", [
+    ((4, 4, 4, 3, 4, 4, 0, 0), "lda"),
+    ((4, 4, 4, 4, 3, 4, 0, 0), "ldb"),
+    ((4, 4, 4, 4, 4, 3, 0, 0), "ldc"),
+    ((4, 4, 4, 3, 4, 4, 0, 1), "lda"),          # column-major A needs lda >= M
+    ((4, 4, 8, 8, 7, 4, 1, 2), "ldb"),          # column-major B needs ldb >= K
+    ((-1, 4, 4, 4, 4, 4, 0, 0), "negative"),
+    ((4, 4, 4, 4, 4, 4, 9, 0), "dtype"),
+    ((4, 4, 4, 4, 4, 4, 0, 4), "layout"),
+    ((1 << 31, 4, 4, 4, 4, 4, 0, 0), "2^31"),
+])
+def test_plan_rejects_invalid_arguments(args, msg):
+    with pytest.raises(mh.GemmError) as e:
+        mh.gemm_plan(*args)
+    assert msg in str(e.value)
+
+
+def test_run_rejects_null_plan_and_describe_null():
+    lib = ctypes.CDLL(mh.LIB_PATH)
+    lib.gemm_run.argtypes = [ctypes.c_void_p] * 5
+    assert lib.gemm_run(None, None, None, None, None) == mh.GEMM_ERR_INVALID_ARG
+    lib.gemm_plan_describe.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert lib.gemm_plan_describe(None, None) == mh.GEMM_ERR_INVALID_ARG
+    lib.gemm_destroy.argtypes = [ctypes.c_void_p]
+    lib.gemm_destroy(None)  # NULL is ignored
+
+
+def test_empty_extents_plan_to_no_kernel():
+    for M, N, K in [(0, 3, 3), (3, 0, 3), (3, 3, 0), (0, 0, 0)]:
+        d = _plan(M, N, K, mh.GEMM_BF16_BF16, lda=max(K, 1), ldb=max(N, 1), ldc=max(N, 1))
+        assert d["kind"] == mh.GEMM_KIND_NONE
+
+
+def test_leading_dimension_only_checked_when_operand_has_elements():
+    d = _plan(5, 5, 0, mh.GEMM_F16_F16, lda=0, ldb=0, ldc=5)
+    assert d["kind"] == mh.GEMM_KIND_NONE
+
+
+def test_the_pages_two_by_two_example():
+    """64 x 64 as tiles of 32 x 32 -> a 2 x 2 grid ("CUDA tile", 2.1)."""
+    d = _plan(64, 64, 64, mh.GEMM_F32_F32)
+    assert (d["kind"], d["bm"], d["bn"]) == (mh.GEMM_KIND_FMA, 32, 32)
+    assert (d["grid_x"], d["grid_y"]) == F.launch_grid(64, 64, 32, 32) == (2, 2)
+
+
+@pytest.mark.parametrize("M,N,K,dtype,layout", [
+    (1024, 1024, 1024, mh.GEMM_F16_F16, 0),
+    (1000, 1000, 1000, mh.GEMM_F16_F16, 0),
+    (2048, 2048, 2048, mh.GEMM_F16_F32, 2),
+    (4096, 4096, 4096, mh.GEMM_BF16_BF16, 0),
+    (16, 8192, 8192, mh.GEMM_BF16_F32, 0),
+    (333, 777, 5, mh.GEMM_F32_F32, 3),
+])
+def test_grid_and_lds_follow_the_formulas(M, N, K, dtype, layout):
+    d = _plan(M, N, K, dtype, layout)
+    assert (d["grid_x"], d["grid_y"]) == F.launch_grid(M, N, d["bm"], d["bn"])
+    elem = 4 if dtype == mh.GEMM_F32_F32 else 2
+    formula = F.smem_bytes(d["bm"], d["bn"], d["bk"], elem, d["stages"])
+    if d["kind"] == mh.GEMM_KIND_MFMA:
+        assert d["lds_bytes"] == formula          # swizzled, no padding
+    else:
+        assert formula <= d["lds_bytes"] <= formula * 1.2   # k-rows padded by 4 floats
+    assert d["lds_bytes"] <= 160 * 1024
+    assert d["cus"] > 0
+
+
+def test_per_shape_regimes():
+    """Small grids take small tiles to fill the compute units; the largest square
+    shape takes the largest tile ("GPU Kernel 的 Tile、Grid、Wave 与 Launch Overhead",
+    per-shape choices: fewer, bigger workers once there are enough of them)."""
+    small = _plan(1024, 1024, 1024, mh.GEMM_F16_F16)
+    mid = _plan(2048, 2048, 2048, mh.GEMM_F16_F32, 2)
+    big = _plan(4096, 4096, 4096, mh.GEMM_BF16_BF16)
+    assert small["bm"] * small["bn"] < mid["bm"] * mid["bn"] < big["bm"] * big["bn"]
+    for d in (small, mid, big):
+        assert d["grid_x"] * d["grid_y"] >= 256
+
+
+def test_forced_configuration_checks():
+    d = _plan(300, 300, 300, mh.GEMM_BF16_BF16, cfg=(2, 128, 128, 64, 2, 2, 2, 1))
+    assert (d["bm"], d["bn"], d["bk"]) == (128, 128, 64)
+    with pytest.raises(mh.GemmError, match="no compiled variant"):
+        _plan(300, 300, 300, mh.GEMM_BF16_BF16, cfg=(2, 96, 96, 64, 2, 2, 2, 1))
+    with pytest.raises(mh.GemmError, match="input type"):
+        _plan(300, 300, 300, mh.GEMM_F32_F32, cfg=(2, 128, 128, 64, 2, 2, 2, 1))
+    with pytest.raises(mh.GemmError, match="input type"):
+        _plan(300, 300, 300, mh.GEMM_BF16_F32, cfg=(1, 64, 64, 16, 4, 1, 2, 1))
+
+
+def test_last_error_clears_on_success():
+    with pytest.raises(mh.GemmError):
+        mh.gemm_plan(4, 4, 4, 1, 4, 4, 0, 0)
+    assert "lda" in mh.gemm_last_error()
+    p = mh.gemm_plan(4, 4, 4, 4, 4, 4, 0, 0)
+    mh.gemm_destroy(p)
+    assert mh.gemm_last_error() == ""

@@ -1,0 +1,242 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Workload tests run each measured shape at full size in the configuration the planner
+picks (the one the benchmark times) and compare every output the oracle can afford:
+whole matrices up to 1024^3, sampled rows at 2048^3, sampled elements at 4096^3, and
+the whole skinny product.  Then: ragged extents that leave partial tiles in every
+dimension, every compiled variant forced on a ragged shape, every layout, padded
+leading dimensions, misaligned pointers (narrow-load path), bit-exact small-integer
+suites (one pins the round-to-nearest-even epilogue), closed forms, degenerate
+extents and guard bands around C.
+"""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import memory_hierarchy_optimisation_amd as mh
+import oracle
+import synth
+from gemm_cases import check_exact, check_tolerance, oracle_ref, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+HALF_DTYPES = [("f16", "f16"), ("f16", "f32"), ("bf16", "bf16"), ("bf16", "f32")]
+ALL_DTYPES = [("f32", "f32")] + HALF_DTYPES
+LAYOUTS = list(itertools.product((False, True), repeat=2))
+
+
+def _catalogue_for(in_t):
+    """Every compiled configuration for an input type, found by forcing each entry of
+    a small list of known shapes (kept in sync with the planner's catalogue)."""
+    if in_t == "f32":
+        return [(1, 32, 32, 32, 4, 1, 2, 1), (1, 64, 64, 16, 4, 1, 2, 1), (1, 128, 128, 16, 4, 1, 2, 1)]
+    return [(2, 64, 64, 64, 2, 2, 2, 1), (2, 128, 128, 64, 2, 2, 2, 1), (2, 256, 128, 64, 2, 2, 2, 1),
+            (2, 256, 256, 64, 2, 4, 2, 1)]
+
+
+# ---- the measured workloads at full size ---------------------------------------------------
+
+def _workload(name):
+    w = synth.WORKLOADS[name]
+    As, lda, Bs, ldb, _, _ = synth.workload_operands(w)
+    print(f"[workload {name}] M={w.M} N={w.N} K={w.K} {w.dtype}->{w.out} a_col={w.a_col} "
+          f"b_col={w.b_col}", flush=True)
+    return w, As, lda, Bs, ldb
+
+
+@pytest.mark.parametrize("name", ["f32_64", "f16_1024", "f16_1000", "bf16_skinny"])
+def test_workload_whole(name):
+    w, As, lda, Bs, ldb = _workload(name)
+    C, raw, desc = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col)
+    Cref = oracle_ref(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.a_col, w.b_col)
+    check_tolerance(C, Cref, w.out, name)
+
+
+def test_workload_2048_nt_sampled_rows():
+    w, As, lda, Bs, ldb = _workload("f16_2048_nt")
+    C, raw, desc = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col)
+    bm = desc["bm"]
+    rows = sorted({0, 1, w.M - 1} | {t * bm + o for t in range(0, w.M // bm, 3) for o in (0, bm - 1)})
+    for r in rows:
+        Cref = oracle_ref(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.a_col, w.b_col, rows=(r, r + 1))
+        check_tolerance(C[r:r + 1], Cref, w.out, f"row {r}")
+
+
+def test_workload_4096_sampled_elements():
+    w, As, lda, Bs, ldb = _workload("bf16_4096")
+    C, raw, desc = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col)
+    bm, bn = desc["bm"], desc["bn"]
+    rng = np.random.default_rng(0)
+    corners_i = [t * bm + o for t in range(w.M // bm) for o in (0, bm - 1)]
+    corners_j = [t * bn + o for t in range(w.N // bn) for o in (0, bn - 1)]
+    ci, cj = np.meshgrid(corners_i, corners_j, indexing="ij")
+    ii = np.concatenate([ci.reshape(-1), rng.integers(0, w.M, 12000)])
+    jj = np.concatenate([cj.reshape(-1), rng.integers(0, w.N, 12000)])
+    ref = oracle.elements(w.M, w.N, w.K, synth.to_storage_numpy(As), lda, synth.to_storage_numpy(Bs), ldb,
+                          w.dtype, ii, jj)
+    check_tolerance(C[ii, jj], ref, w.out, "sampled elements")
+    # All-ones closed form over the whole output at the same shape: C_ij = K exactly.
+    ones = torch.ones((w.M, w.K), dtype=synth.TORCH_DTYPES[w.dtype])
+    onesb = torch.ones((w.K, w.N), dtype=synth.TORCH_DTYPES[w.dtype])
+    C1, raw1, _ = run_gpu(ones, w.K, onesb, w.N, w.M, w.N, w.K, w.dtype, w.out)
+    assert np.all(C1 == w.K)
+
+
+def test_workload_64_as_two_by_two_tiles():
+    """The 64x64 product as 2 x 2 tiles of 32 x 32 ("CUDA tile", 2.1)."""
+    w, As, lda, Bs, ldb = _workload("f32_64")
+    cfg = (1, 32, 32, 32, 4, 1, 2, 1)
+    C, raw, desc = run_gpu(As, lda, Bs, ldb, 64, 64, 64, "f32", "f32", cfg=cfg)
+    assert (desc["grid_x"], desc["grid_y"]) == (2, 2)
+    check_tolerance(C, oracle_ref(As, lda, Bs, ldb, 64, 64, 64, "f32"), "f32")
+
+
+# ---- ragged extents ------------------------------------------------------------------------
+
+EDGES = [1, 15, 16, 17, 31, 33, 63, 65, 127, 129]
+
+
+@pytest.mark.parametrize("in_t,out_t", ALL_DTYPES)
+def test_ragged_extents(in_t, out_t):
+    rng = np.random.default_rng(5)
+    cases = [(m, n, k) for m in EDGES for n in EDGES for k in (1, 17, 65, 129)]
+    picks = rng.choice(len(cases), 60, replace=False)
+    for idx in picks:
+        M, N, K = cases[idx]
+        for a_col, b_col in LAYOUTS:
+            As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, seed=int(idx))
+            C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col)
+            Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
+            check_tolerance(C, Cref, out_t, f"M={M} N={N} K={K} a_col={a_col} b_col={b_col}")
+
+
+@pytest.mark.parametrize("in_t,out_t", ALL_DTYPES)
+def test_every_variant_every_layout_ragged(in_t, out_t):
+    M, N, K = 300, 270, 200
+    for cfg in _catalogue_for(in_t):
+        for a_col, b_col in LAYOUTS:
+            As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, seed=3)
+            C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, cfg=cfg)
+            assert (desc["bm"], desc["bn"]) == (cfg[1], cfg[2])
+            Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
+            check_tolerance(C, Cref, out_t, f"cfg={cfg} a_col={a_col} b_col={b_col}")
+
+
+@pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
+def test_thousand_cubed_every_layout(in_t, out_t):
+    M = N = K = 1000
+    for a_col, b_col in LAYOUTS:
+        As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, seed=1)
+        C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col)
+        rows = (0, 70)
+        Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col, rows=rows)
+        check_tolerance(C[rows[0]:rows[1]], Cref, out_t, f"a_col={a_col} b_col={b_col}")
+        Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col, rows=(M - 40, M))
+        check_tolerance(C[M - 40:], Cref, out_t, f"last rows a_col={a_col} b_col={b_col}")
+
+
+# ---- leading dimensions and alignment ------------------------------------------------------------
+
+@pytest.mark.parametrize("in_t,out_t", ALL_DTYPES)
+def test_padded_leading_dimensions(in_t, out_t):
+    M, N, K = 200, 136, 264
+    for a_col, b_col in LAYOUTS:
+        lda = (M if a_col else K) + 24
+        ldb = (K if b_col else N) + 8
+        As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, lda=lda, ldb=ldb, seed=2)
+        C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, ldc=N + 40)
+        Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
+        check_tolerance(C, Cref, out_t, f"a_col={a_col} b_col={b_col}")
+
+
+@pytest.mark.parametrize("in_t,out_t", ALL_DTYPES)
+def test_misaligned_pointers_and_odd_leading_dimensions(in_t, out_t):
+    M, N, K = 130, 97, 211
+    for a_col, b_col in LAYOUTS:
+        lda = (M if a_col else K) + 3
+        ldb = (K if b_col else N) + 5
+        As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, lda=lda, ldb=ldb, seed=4)
+        C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, ldc=N + 1,
+                            offset_a=1, offset_b=3, offset_c=1)
+        Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
+        check_tolerance(C, Cref, out_t, f"a_col={a_col} b_col={b_col}")
+
+
+# ---- bit-exact integer suites --------------------------------------------------------------------
+
+@pytest.mark.parametrize("in_t,out_t", HALF_DTYPES)
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_exact_sparse_sums(in_t, out_t, a_col, b_col):
+    """Entries in {-1, 0, 1}; B column j nonzero only where (k + j) % period == 0, so
+    |C| <= ceil(K / period) is exact in the output type and every slab contributes."""
+    M, N, K = 257, 190, 1000
+    limit = 256 if out_t == "bf16" else 2048
+    period = -(-K // limit)
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, dist="sparse_pm1",
+                                            period=period, seed=8)
+    C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col)
+    Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
+    check_exact(raw, Cref, out_t)
+
+
+@pytest.mark.parametrize("in_t,out_t", ALL_DTYPES)
+def test_exact_dense_small_integers_rounded_once(in_t, out_t):
+    """Dense integers in [-4, 4]: every fp32 partial sum is exact (|sum| <= 16K < 2^24),
+    so the only rounding is the final cast: the output must equal the oracle's
+    round-to-nearest-even of the exact sum, bit for bit."""
+    for (M, N, K), cfg in [((320, 260, 1024), None), ((64, 64, 4096), None)]:
+        for a_col, b_col in [(False, False), (False, True)]:
+            As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, dist="int", r=4, seed=9)
+            C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, cfg=cfg)
+            Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
+            check_exact(raw, Cref, out_t)
+
+
+# ---- closed forms ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["f32_64", "f16_1024", "f16_1000", "f16_2048_nt", "bf16_skinny"])
+def test_closed_forms_at_workload_shapes(name):
+    w = synth.WORKLOADS[name]
+    # all ones: C_ij = K exactly in every output type used
+    As, lda, Bs, ldb, _, _ = synth.operands(w.M, w.N, w.K, w.dtype, w.a_col, w.b_col, dist="ones")
+    C, raw, _ = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col)
+    assert np.all(C == w.K)
+    # identity on the right (B = I when K == N): C = A exactly
+    if w.K == w.N:
+        As, lda, Bs, ldb, A, _ = synth.operands(w.M, w.N, w.K, w.dtype, w.a_col, w.b_col,
+                                                dist="uniform", dist_b="identity", seed=1)
+        C, raw, _ = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col)
+        assert np.array_equal(C, A.to(torch.float64).numpy())
+    # permutation on the left (A = P when M == K): rows of B permuted exactly
+    if w.M == w.K:
+        As, lda, Bs, ldb, P, B = synth.operands(w.M, w.N, w.K, w.dtype, w.a_col, w.b_col,
+                                                dist="perm", dist_b="uniform", seed=2)
+        C, raw, _ = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col)
+        p = P.to(torch.float64).numpy().argmax(axis=1)
+        assert np.array_equal(C, B.to(torch.float64).numpy()[p])
+
+
+# ---- degenerate extents ------------------------------------------------------------------------
+
+@pytest.mark.parametrize("in_t,out_t", ALL_DTYPES)
+def test_degenerate_extents(in_t, out_t):
+    # M = 0 or N = 0: nothing is written (the guard bands check that)
+    for M, N, K in [(0, 5, 7), (6, 0, 7), (0, 0, 0)]:
+        As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t)
+        C, raw, desc = run_gpu(As, max(lda, 1), Bs, max(ldb, 1), M, N, K, in_t, out_t, ldc=max(N, 1))
+        assert desc["kind"] == mh.GEMM_KIND_NONE
+    # K = 0: C is the empty sum, zero everywhere
+    M, N = 33, 45
+    empty = torch.zeros((0,), dtype=synth.TORCH_DTYPES[in_t])
+    C, raw, desc = run_gpu(empty, 1, empty, N, M, N, 0, in_t, out_t, ldc=N + 3)
+    assert np.all(C == 0)
+
+
+def test_single_element_and_single_row():
+    for in_t, out_t in ALL_DTYPES:
+        for M, N, K in [(1, 1, 1), (1, 1, 4096), (1, 4096, 1), (4096, 1, 8), (1, 300, 700)]:
+            As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, seed=M + N + K)
+            C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t)
+            check_tolerance(C, oracle_ref(As, lda, Bs, ldb, M, N, K, in_t), out_t, f"{M}x{N}x{K}")
