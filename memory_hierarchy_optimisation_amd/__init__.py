@@ -9,6 +9,12 @@ memory and streams.
 import ctypes
 import os
 
+# torch is imported before the library is loaded: torch carries its own HIP and HSA
+# runtimes, and the library's dependency on libamdhip64 then binds to the copy torch
+# already mapped.  Loading the library first would bring a second HIP runtime into
+# the process, whose streams, allocations and synchronisation the other cannot see.
+import torch  # noqa: F401
+
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmhgemm.so")
 
@@ -41,6 +47,19 @@ class GemmError(RuntimeError):
         self.code = code
 
 
+def hip_runtimes_mapped():
+    """Paths of the HIP runtime libraries mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as fh:
+            for line in fh:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return sorted(paths)
+
+
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
@@ -60,6 +79,10 @@ def _load():
     lib.gemm_last_error.restype = ctypes.c_char_p
     lib.gemm_plan_describe.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_plan_describe.restype = i32
+    runtimes = hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise ImportError("more than one HIP runtime is mapped into this process "
+                          f"({runtimes}); import torch before loading libmhgemm")
     return lib
 
 

@@ -144,3 +144,8 @@ def test_last_error_clears_on_success():
     p = mh.gemm_plan(4, 4, 4, 4, 4, 4, 0, 0)
     mh.gemm_destroy(p)
     assert mh.gemm_last_error() == ""
+
+
+def test_one_hip_runtime_in_the_process():
+    """The library shares torch's HIP runtime instead of mapping a second one."""
+    assert len(mh.hip_runtimes_mapped()) == 1
