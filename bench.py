@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the tiled GEMM on one MI355X.
+
+One step = one call of the planned product (gemm_run) on one batch of synthetic
+operands already resident in HBM.  The headline workload is the bf16 4096^3 product
+(bf16 output, fp32 accumulation): value = 2*M*N*K / (wall seconds per step), in
+TFLOP/s.  The other measured shapes are reported under "per_shape" with their
+roofline fraction: min(peak, intensity * 8 TB/s), where intensity counts each
+operand once (2MNK over the bytes of A, B and C).
+
+Operands rotate over enough copies that the working set exceeds the 256 MB
+Infinity Cache, so the bandwidth-bound shape streams from HBM.
+
+Prints ONE JSON line on stdout; everything else goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HEADLINE = "bf16_4096"
+PER_SHAPE = ["f32_64", "f16_1024", "f16_1000", "f16_2048_nt", "bf16_4096", "bf16_skinny"]
+# Published dense peaks of the MI355X (TFLOP/s) and its HBM bandwidth (GB/s).
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+HBM_GBPS = 8000.0
+ELEM = {"f32": 4, "f16": 2, "bf16": 2}
+ROTATE_BYTES = 512 << 20       # working set of rotated operand copies, > 256 MB cache
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_digest():
+    """Digest of the kernel sources; profile figures carry it so stale ones are ignored."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "memory_hierarchy_optimisation_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(name.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w):
+    flops = 2.0 * w.M * w.N * w.K
+    nbytes = w.M * w.K * ELEM[w.dtype] + w.K * w.N * ELEM[w.dtype] + w.M * w.N * ELEM[w.out]
+    return flops, nbytes
+
+
+def roofline_of(w):
+    flops, nbytes = algorithmic(w)
+    ai = flops / nbytes
+    peak = PEAK_TFLOPS[w.dtype]
+    roof = min(peak, ai * HBM_GBPS / 1000.0)
+    bound = "hbm" if ai * HBM_GBPS / 1000.0 < peak else ("mfma" if w.dtype != "f32" else "alu")
+    return ai, roof, bound
+
+
+def measure(name, steps, warmup, per_call=False):
+    """Time `steps` calls after `warmup` untimed calls.  Returns a dict of figures."""
+    import torch
+
+    import memory_hierarchy_optimisation_amd as mh
+    import synth
+
+    w = synth.WORKLOADS[name]
+    As, lda, Bs, ldb, _, _ = synth.workload_operands(w)
+    pair = As.numel() * As.element_size() + Bs.numel() * Bs.element_size()
+    copies = max(1, min(256, math.ceil(ROTATE_BYTES / pair)))
+    A0, B0 = As.cuda(), Bs.cuda()
+    As_dev = [A0] + [A0.clone() for _ in range(copies - 1)]
+    Bs_dev = [B0] + [B0.clone() for _ in range(copies - 1)]
+    C = torch.empty((w.M, w.N), dtype=synth.TORCH_DTYPES[w.out], device="cuda")
+    code = mh.DTYPE_OF[(w.dtype, w.out)]
+    layout = (mh.GEMM_A_COL if w.a_col else 0) | (mh.GEMM_B_COL if w.b_col else 0)
+    plan = mh.gemm_plan(w.M, w.N, w.K, lda, ldb, w.N, code, layout)
+    desc = mh.gemm_plan_describe(plan)
+    stream = torch.cuda.current_stream()
+    try:
+        for i in range(warmup):
+            mh.gemm_run(plan, As_dev[i % copies], Bs_dev[i % copies], C, stream)
+        torch.cuda.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for i in range(steps):
+            mh.gemm_run(plan, As_dev[i % copies], Bs_dev[i % copies], C, stream)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        event_ms = ev0.elapsed_time(ev1) / steps
+        calls = []
+        if per_call:
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(steps)]
+            for i, (a, b) in enumerate(evs):
+                a.record(stream)
+                mh.gemm_run(plan, As_dev[i % copies], Bs_dev[i % copies], C, stream)
+                b.record(stream)
+            torch.cuda.synchronize()
+            calls = sorted(a.elapsed_time(b) for a, b in evs)
+    finally:
+        mh.gemm_destroy(plan)
+    flops, nbytes = algorithmic(w)
+    ai, roof, bound = roofline_of(w)
+    ms_step = wall * 1000.0 / steps
+    out = {
+        "workload": name, "M": w.M, "N": w.N, "K": w.K, "in": w.dtype, "out": w.out,
+        "layout": ("A col" if w.a_col else "A row") + (", B col" if w.b_col else ", B row"),
+        "tile": f"{desc['bm']}x{desc['bn']}x{desc['bk']}", "kind": desc["kind"],
+        "grid": desc["grid_x"] * desc["grid_y"] * desc["grid_z"], "rotated_copies": copies,
+        "ms_per_step": ms_step, "kernel_ms_event": event_ms,
+        "tflops": flops / (ms_step / 1000.0) / 1e12,
+        "kernel_tflops": flops / (event_ms / 1000.0) / 1e12,
+        "kernel_gbps": nbytes / (event_ms / 1000.0) / 1e9,
+        "intensity": ai, "bound": bound, "roofline_tflops": roof,
+    }
+    out["frac_of_roofline"] = out["kernel_tflops"] / roof
+    if calls:
+        k = len(calls)
+        out["kernel_ms_p10_p50_p90"] = [calls[k // 10], calls[k // 2], calls[(9 * k) // 10]]
+    return out
+
+
+def copy_reference(nbytes=512 << 20):
+    """One elementwise device kernel of known traffic (reads and writes nbytes), run
+    after the timed region so a counter run can scale FETCH_SIZE / WRITE_SIZE."""
+    import torch
+
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy reference: {nbytes} bytes read and written by one elementwise kernel")
+
+
+def traffic_for(name):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_traffic(fetch_csv, write_csv, name, digest, out_path):
+    """Write the HBM-traffic summary of one workload's GEMM kernel from two rocprofv3
+    counter runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what
+    the same counter reads for the copy reference kernel of known traffic."""
+    import csv
+
+    import synth
+
+    def per_kernel(path):
+        acc = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+    fetch, n_fetch = per_kernel(fetch_csv)
+    write, n_write = per_kernel(write_csv)
+    gemm = [k for k in fetch if "mhg::" in k and "gemm" in k]
+    ref = [k for k in fetch if "elementwise" in k and "Unary" in k]
+    if len(gemm) != 1 or len(ref) != 1:
+        raise SystemExit(f"expected one GEMM kernel and one copy reference, got {gemm} / {ref}")
+    g, c = gemm[0], ref[0]
+    ref_kib = (512 << 20) / 1024.0
+    f_scale, w_scale = ref_kib / fetch[c], ref_kib / write[c]
+    w = synth.WORKLOADS[name]
+    _, alg = algorithmic(w)
+    traffic = fetch[g] * f_scale * 1024 + write[g] * w_scale * 1024
+    lines = [
+        f"# HBM traffic per launch of the {name} GEMM kernel (rocprofv3 counters)",
+        f"kernel: {g}",
+        f"kernel_source_digest: {digest}",
+        f"fetch_size_kib_per_dispatch: {fetch[g]:.1f}  (mean of {n_fetch[g]} dispatches)",
+        f"write_size_kib_per_dispatch: {write[g]:.1f}  (mean of {n_write[g]} dispatches)",
+        f"copy_reference_fetch_kib: {fetch[c]:.1f}  (kernel reads 524288 KiB)",
+        f"copy_reference_write_kib: {write[c]:.1f}  (kernel writes 524288 KiB)",
+        f"fetch_scale: {f_scale:.5f}",
+        f"write_scale: {w_scale:.5f}",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"algorithmic_bytes_per_launch: {alg:.0f}",
+        f"traffic_over_algorithmic: {traffic / alg:.3f}",
+    ]
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    log("\n".join(lines))
+
+
+def cpu_baseline(name, seconds):
+    """The oracle as it stands, on the host cores, over the first rows of the product."""
+    import oracle
+    import synth
+
+    w = synth.WORKLOADS[name]
+    As, lda, Bs, ldb, _, _ = synth.workload_operands(w)
+    a = synth.to_storage_numpy(As)
+    b = synth.to_storage_numpy(Bs)
+    probe = min(w.M, 16)
+    t0 = time.perf_counter()
+    oracle.gemm(w.M, w.N, w.K, a, lda, b, ldb, w.dtype, a_col=w.a_col, b_col=w.b_col, rows=(0, probe))
+    t_probe = time.perf_counter() - t0
+    rows = int(max(probe, min(w.M, probe * seconds / max(t_probe, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.gemm(w.M, w.N, w.K, a, lda, b, ldb, w.dtype, a_col=w.a_col, b_col=w.b_col, rows=(0, rows))
+    t = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {
+        "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} {w.dtype} product "
+                  f"({rows * w.N} of {w.M * w.N} outputs, {t:.1f} s, binary64 triple loop)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=HEADLINE, help="workload timed as the headline")
+    ap.add_argument("--no-per-shape", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="after timing, run one elementwise kernel of known traffic (counter scale)")
+    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "DIGEST"),
+                    help="write profiles/traffic_<workload>.txt from two counter runs and exit")
+    args = ap.parse_args()
+    if args.summarize_traffic:
+        f, wcsv, digest = args.summarize_traffic
+        summarize_traffic(f, wcsv, args.workload, digest,
+                          os.path.join(ROOT, "profiles", f"traffic_{args.workload}.txt"))
+        return
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU: this build runs the product on a single MI355X "
+            f"(--gpus {args.gpus} is not supported)")
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; headline {args.workload}")
+
+    head = measure(args.workload, args.steps, args.warmup, per_call=True)
+    log(f"[bench] headline {head['workload']}: {head['tflops']:.1f} TFLOP/s "
+        f"({head['ms_per_step'] * 1000:.1f} us/step, kernel {head['kernel_ms_event'] * 1000:.1f} us)")
+    shapes = []
+    if not args.no_per_shape:
+        for name in PER_SHAPE:
+            r = head if name == args.workload else measure(name, 100, 10, per_call=True)
+            shapes.append(r)
+            log(f"[bench] {name}: {r['kernel_tflops']:.1f} TFLOP/s, {r['kernel_gbps']:.0f} GB/s, "
+                f"{100 * r['frac_of_roofline']:.1f}% of the {r['bound']} roofline, tile {r['tile']}")
+    if args.copy_reference:
+        copy_reference()
+
+    import synth
+    w = synth.WORKLOADS[args.workload]
+    flops, _ = algorithmic(w)
+    achieved = head["kernel_tflops"]
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = traffic_for(args.workload)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores ...")
+        cpu = cpu_baseline(args.workload, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value'] * 1000:.2f} GFLOP/s on {cpu['cores']} threads")
+    line = {
+        "metric": f"GEMM TFLOP/s, {w.M}x{w.N}x{w.K} {w.dtype} in, fp32 accumulate, {w.out} out",
+        "value": head["tflops"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.note, "M": w.M, "N": w.N, "K": w.K, "in": w.dtype, "out": w.out,
+                   "layout": head["layout"], "tile": head["tile"], "grid": head["grid"],
+                   "rotated_copies": head["rotated_copies"]},
+        "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
+        "cpu_baseline": cpu,
+        "kernel_source_digest": kernel_source_digest(),
+        "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                      for r in shapes],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
