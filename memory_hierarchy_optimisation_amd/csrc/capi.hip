@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -17,6 +18,9 @@ namespace mhg {
 hipError_t launch_fma(int launcher, const LaunchArgs &p, hipStream_t s);
 hipError_t launch_mfma(int launcher, const LaunchArgs &p, hipStream_t s);
 hipError_t launch_fill(const LaunchArgs &p, hipStream_t s);
+hipError_t launch_ring(int launcher, const LaunchArgs &p, hipStream_t s);
+bool ring_supported(const LaunchArgs &p, int bm, int bn);
+hipError_t launch_big(const LaunchArgs &p, hipStream_t s);
 }  // namespace mhg
 
 struct gemm_plan_s {
@@ -122,12 +126,27 @@ int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stre
     const int elems16 = 16 / mhg::elem_bytes(d.in_code);
     a.vec_a = (reinterpret_cast<uintptr_t>(A) % 16 == 0) && (d.lda % elems16 == 0);
     a.vec_b = (reinterpret_cast<uintptr_t>(B) % 16 == 0) && (d.ldb % elems16 == 0);
+    // four output elements per store: 16 bytes of fp32 or 8 bytes of fp16 / bf16
+    const int out_bytes = mhg::elem_bytes(d.out_code);
+    a.c_vec = (reinterpret_cast<uintptr_t>(C) % (4 * out_bytes) == 0) && (d.ldc % 4 == 0);
     int count;
-    const mhg::Variant &v = mhg::catalogue(&count)[d.variant];
-    switch (d.cfg.kind) {
-      case GEMM_KIND_FMA: e = mhg::launch_fma(v.launcher, a, s); break;
-      case GEMM_KIND_MFMA: e = mhg::launch_mfma(v.launcher, a, s); break;
-      default: e = hipErrorInvalidValue; break;
+    const mhg::Variant *cat = mhg::catalogue(&count);
+    const mhg::Variant *v = &cat[d.variant];
+    if (v->fallback >= 0 && !mhg::ring_supported(a, v->cfg.bm, v->cfg.bn)) {
+      v = mhg::variant_of_launcher(v->fallback);   // same tile, register-staged: any alignment
+      a.gm = int((d.M + v->cfg.bm - 1) / v->cfg.bm);
+      a.gn = int((d.N + v->cfg.bn - 1) / v->cfg.bn);
+      a.group_m = std::max(1, std::min(a.gm, 4));
+    }
+    switch (v->launcher) {
+      case mhg::L_FMA_32: case mhg::L_FMA_64: case mhg::L_FMA_128:
+        e = mhg::launch_fma(v->launcher, a, s); break;
+      case mhg::L_RING_256x256_W4: case mhg::L_RING_256x256_W8: case mhg::L_RING_128x128_W4:
+        e = mhg::launch_ring(v->launcher, a, s); break;
+      case mhg::L_BIG_256:
+        e = mhg::launch_big(a, s); break;
+      default:
+        e = mhg::launch_mfma(v->launcher, a, s); break;
     }
   }
   if (e != hipSuccess) {

@@ -34,6 +34,20 @@ __device__ __forceinline__ f32x4 mfma16(HalfF16, u32x4 a, u32x4 b, f32x4 acc) {
                                                 __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
 }
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// One 32x32x16 matrix multiply-accumulate on a wave: acc += A(32x16) * B(16x32).
+// Lane l holds A row (l % 32), k = 8*(l/32) .. +7 and B column (l % 32) over the same
+// k; accumulator element r holds row 8*(r/4) + 4*(l/32) + r%4 of column l % 32.
+__device__ __forceinline__ f32x16 mfma32(HalfBF16, u32x4 a, u32x4 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(HalfF16, u32x4 a, u32x4 b, f32x16 acc) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
+}
+
 // LDS transpose read of four 16-bit elements.  Within each group of 16 lanes, lane t
 // receives element (t & 3) of the 8-byte rows addressed by lanes 4q + (t >> 2),
 // q = 0..3: a 4 x 16 block of a row-major tile comes back column by column.
@@ -60,6 +74,38 @@ __device__ __forceinline__ void tile_of(int bid, int gm, int gn, int group_m, in
   const int in = logical - g * per_group;
   tm = first + in % gsz;
   tn = in / gsz;
+}
+
+// Store four consecutive elements C[idx .. idx+3] from fp32 values, converting to the
+// output type (round to nearest even).  `vec`: the four are inside the matrix and the
+// address is aligned for one 8-byte (16-bit types) or 16-byte (fp32) store; otherwise
+// element `e` is stored only when e < n_in.
+__device__ __forceinline__ void store_out4(void *C, int64_t idx, f32x4 v, int out_code, bool vec, int n_in) {
+  if (out_code == E_F32) {
+    float *c = reinterpret_cast<float *>(C) + idx;
+    if (vec) {
+      *reinterpret_cast<f32x4 *>(c) = v;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < n_in) c[e] = v[e];
+    }
+    return;
+  }
+  uint16_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    h[e] = out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)v[e])
+                             : __builtin_bit_cast(uint16_t, (__bf16)v[e]);
+  uint16_t *c = reinterpret_cast<uint16_t *>(C) + idx;
+  if (vec) {
+    *reinterpret_cast<u32x2 *>(c) = u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16),
+                                          uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (e < n_in) c[e] = h[e];
+  }
 }
 
 // fp32 -> output element, round to nearest even for the 16-bit types.

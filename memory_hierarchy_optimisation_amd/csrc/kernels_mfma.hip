@@ -19,8 +19,8 @@
 // Global loads are 16 bytes per lane along the contiguous dimension ("Tiling 策略与
 // 内存层次优化", memory coalescing and the 128-bit vector loads of the walk-through).
 // Loads that would leave the matrix are replaced by zeros ("CUDA tile", 4: zero
-// padding is the identity of the sum); a chunk that straddles the edge is read
-// element by element.  LDS chunk positions are XOR-swizzled by row (same page, bank
+// padding is the identity of the sum) without branching; operands that cannot take
+// 16-byte loads use an instantiation that reads element by element.  LDS chunk positions are XOR-swizzled by row (same page, bank
 // conflicts and swizzling: bank index = (row XOR column) mod banks).
 #include "device.h"
 
@@ -43,9 +43,29 @@ __device__ __forceinline__ int mn_off(int krow, int chunk) {
   return krow * (NCH * 16) + ((chunk ^ (((krow & 3) << 1) & (NCH - 1))) << 4);
 }
 
+// Buffer resource over `bytes` bytes from `base` (raw addressing, stride 0).  Loads
+// whose offset lies at or beyond the range return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Offset that a load takes for a chunk outside the matrix: beyond every resource range.
+constexpr uint32_t kOutside = 0x80000000u;
+
 // One operand's share of a K slab: R rows of C-tile extent (BM for A, BN for B),
-// K-contiguous (KC) or not, staged by NT threads.
-template <int R, bool KC, int NT>
+// K-contiguous (KC) or not, staged by NT threads.  Chunk q of the slab is 8
+// consecutive elements along the storage's contiguous dimension.
+//
+// VEC: 16-byte buffer loads.  The host selects it only when the base is 16-byte
+// aligned and the leading dimension and the contiguous extent are multiples of 8
+// elements, so every chunk lies wholly inside or wholly outside the matrix.  Each
+// slab gets a buffer resource whose base is the slab's origin in storage; a chunk's
+// byte offset from that origin does not change from slab to slab, and a chunk
+// outside the matrix takes the out-of-range offset, which loads zeros.  No branch or
+// select touches the loaded value, so the compiler can leave the load in flight
+// across the matrix instructions and wait only before the LDS store.
+// !VEC: element loads with per-element masks (unaligned or ragged storage).
+template <int R, bool KC, int NT, bool VEC>
 struct OperandTile {
   static constexpr int CHUNKS = R * BK / 8;
   static constexpr int PER = CHUNKS / NT;
@@ -54,39 +74,63 @@ struct OperandTile {
   static_assert(KC || (NCH & (NCH - 1)) == 0, "chunks per row must be a power of two");
 
   u32x4 reg[PER];
+  const uint16_t *base;   // operand storage
+  int64_t ld;
+  int64_t mn_lim, K;
+  int mn0;                // m0 or n0 of this workgroup
+  uint32_t off[VEC ? PER : 1];   // byte offset of chunk i from the slab origin
+  bool mn_ok[VEC ? PER : 1];     // chunk i's m (or n) coordinate lies inside the matrix
 
-  // Issue the global loads of the slab starting at k0 into registers.
-  //   g: storage; ld: leading dimension; mn_lim: M (A) or N (B); base: m0 or n0.
-  __device__ __forceinline__ void load(const uint16_t *__restrict__ g, int64_t ld, int64_t mn_lim,
-                                       int64_t K, int base, int k0, int vec) {
+  __device__ __forceinline__ OperandTile(const uint16_t *g, int64_t ld_, int64_t mn_lim_, int64_t K_, int mn0_)
+      : base(g), ld(ld_), mn_lim(mn_lim_), K(K_), mn0(mn0_) {
+    if (VEC) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int q = threadIdx.x + i * NT;
-      int64_t row, col, row_lim, col_lim;
-      if (KC) {
-        row = base + q / 8;           // m or n
-        col = k0 + 8 * (q % 8);       // k, contiguous
-        row_lim = mn_lim;
-        col_lim = K;
-      } else {
-        row = k0 + q / NCH;           // k
-        col = base + 8 * (q % NCH);   // m or n, contiguous
-        row_lim = K;
-        col_lim = mn_lim;
+      for (int i = 0; i < PER; ++i) {
+        const int q = threadIdx.x + i * NT;
+        // KC: storage row = m (or n), column = k.  Else: storage row = k, column = m (n).
+        const int r = KC ? q / 8 : q / NCH;
+        const int c = KC ? 8 * (q % 8) : 8 * (q % NCH);
+        off[i] = uint32_t((int64_t(r) * ld + c) * 2);
+        mn_ok[i] = KC ? (mn0 + r < mn_lim) : (mn0 + c < mn_lim);
       }
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < row_lim) {
-        const uint16_t *src = g + row * ld + col;
-        if (vec && col + 8 <= col_lim) {
-          v = *reinterpret_cast<const u32x4 *>(src);
-        } else if (col < col_lim) {
-          uint32_t h[8];
+    }
+  }
+
+  // k coordinate within the slab of chunk i
+  __device__ __forceinline__ int kin(int i) const {
+    const int q = threadIdx.x + i * NT;
+    return KC ? 8 * (q % 8) : q / NCH;
+  }
+
+  // Issue the global loads of the slab starting at k0 into registers.  `full`: the
+  // whole slab lies inside the matrix (uniform across the workgroup).
+  __device__ __forceinline__ void load(int k0, bool full) {
+    if (VEC) {
+      // slab origin: (row m0/n0, column k0) for KC storage, (row k0, column m0/n0) otherwise
+      const uint16_t *origin = KC ? base + int64_t(mn0) * ld + k0 : base + int64_t(k0) * ld + mn0;
+      const __amdgpu_buffer_rsrc_t rsrc = make_rsrc(origin, 0x7fffffffu);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = (col + e < col_lim) ? src[e] : 0u;
-          v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+      for (int i = 0; i < PER; ++i) {
+        const bool in = full || (mn_ok[i] && k0 + kin(i) < K);
+        reg[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, in ? off[i] : kOutside, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int q = threadIdx.x + i * NT;
+        const int64_t row = KC ? mn0 + q / 8 : k0 + q / NCH;
+        const int64_t col = KC ? k0 + 8 * (q % 8) : mn0 + 8 * (q % NCH);
+        const int64_t row_lim = KC ? mn_lim : K, col_lim = KC ? K : mn_lim;
+        uint32_t h[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const bool in = row < row_lim && col + e < col_lim;
+          const uint16_t *src = in ? base + row * ld + col + e : base;
+          const uint32_t x = *src;
+          h[e] = in ? x : 0u;
         }
+        reg[i] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
       }
-      reg[i] = v;
     }
   }
 
@@ -94,8 +138,8 @@ struct OperandTile {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       const int q = threadIdx.x + i * NT;
-      const int off = KC ? kc_off(q / 8, q % 8) : mn_off<NCH>(q / NCH, q % NCH);
-      *reinterpret_cast<u32x4 *>(lds + off) = reg[i];
+      const int off_lds = KC ? kc_off(q / 8, q % 8) : mn_off<NCH>(q / NCH, q % NCH);
+      *reinterpret_cast<u32x4 *>(lds + off_lds) = reg[i];
     }
   }
 
@@ -117,7 +161,7 @@ struct OperandTile {
   }
 };
 
-template <class H, int BM, int BN, int WM, int WN, bool A_KC, bool B_KC>
+template <class H, int BM, int BN, int WM, int WN, bool A_KC, bool B_KC, bool VEC>
 __global__ void __launch_bounds__(WM * WN * 64)
 mfma_gemm(LaunchArgs p) {
   constexpr int NT = WM * WN * 64;
@@ -134,8 +178,10 @@ mfma_gemm(LaunchArgs p) {
   const uint16_t *__restrict__ A = static_cast<const uint16_t *>(p.A);
   const uint16_t *__restrict__ B = static_cast<const uint16_t *>(p.B);
 
-  OperandTile<BM, A_KC, NT> ta;
-  OperandTile<BN, B_KC, NT> tb;
+  OperandTile<BM, A_KC, NT, VEC> ta(A, p.lda, p.M, p.K, m0);
+  OperandTile<BN, B_KC, NT, VEC> tb(B, p.ldb, p.N, p.K, n0);
+  // Slabs lie wholly inside the matrix when the tile does and k0 + BK <= K.
+  const bool tile_in = (m0 + BM <= p.M) && (n0 + BN <= p.N);
   f32x4 acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -143,8 +189,8 @@ mfma_gemm(LaunchArgs p) {
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int KT = int((p.K + BK - 1) / BK);
-  ta.load(A, p.lda, p.M, p.K, m0, 0, p.vec_a);
-  tb.load(B, p.ldb, p.N, p.K, n0, 0, p.vec_b);
+  ta.load(0, tile_in && BK <= p.K);
+  tb.load(0, tile_in && BK <= p.K);
   ta.store(smem);
   tb.store(smem + A_BYTES);
   __syncthreads();
@@ -153,8 +199,10 @@ mfma_gemm(LaunchArgs p) {
     const char *cur = smem + (t & 1) * STAGE;
     const bool more = t + 1 < KT;
     if (more) {
-      ta.load(A, p.lda, p.M, p.K, m0, (t + 1) * BK, p.vec_a);
-      tb.load(B, p.ldb, p.N, p.K, n0, (t + 1) * BK, p.vec_b);
+      const int k1 = (t + 1) * BK;
+      const bool full = tile_in && k1 + BK <= p.K;
+      ta.load(k1, full);
+      tb.load(k1, full);
     }
 #pragma unroll
     for (int s = 0; s < BK / 32; ++s) {
@@ -166,7 +214,7 @@ mfma_gemm(LaunchArgs p) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(H{}, af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(H{}, bf[j], af[i], acc[i][j]);
     }
     if (more) {
       char *nxt = smem + ((t + 1) & 1) * STAGE;
@@ -176,31 +224,44 @@ mfma_gemm(LaunchArgs p) {
     __syncthreads();
   }
 
-  // Epilogue: lane holds rows 4*(lane/16) .. +3 of column lane%16 of each block.
+  // The instructions take B's fragment first and A's second, so each accumulator holds
+  // the transposed 16 x 16 block: lane l has C[row 16 i + l % 16][cols 16 j + 4 (l / 16) .. +3]
+  // of the wave's block, four consecutive columns written as one 8- or 16-byte piece.
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int64_t row = m0 + wm * WTM + i * 16 + (lane & 15);
+    if (row >= p.M) continue;
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
-      const int64_t col = n0 + wn * WTN + j * 16 + (lane & 15);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + r;
-        if (row < p.M && col < p.N) store_out(p.C, row * p.ldc + col, acc[i][j][r], p.out_code);
-      }
+      const int64_t col = n0 + wn * WTN + j * 16 + 4 * (lane >> 4);
+      const int64_t n_in = p.N - col;
+      if (n_in <= 0) continue;
+      store_out4(p.C, row * p.ldc + col, acc[i][j], p.out_code, p.c_vec && n_in >= 4, int(n_in));
     }
+  }
 }
 
 template <class H, int BM, int BN, int WM, int WN>
 hipError_t launch_tiles(const LaunchArgs &p, hipStream_t s) {
   const dim3 grid(unsigned(p.gm) * unsigned(p.gn)), block(WM * WN * 64);
-  if (!p.a_col && !p.b_col)
-    hipLaunchKernelGGL((mfma_gemm<H, BM, BN, WM, WN, true, false>), grid, block, 0, s, p);
-  else if (!p.a_col && p.b_col)
-    hipLaunchKernelGGL((mfma_gemm<H, BM, BN, WM, WN, true, true>), grid, block, 0, s, p);
-  else if (p.a_col && !p.b_col)
-    hipLaunchKernelGGL((mfma_gemm<H, BM, BN, WM, WN, false, false>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((mfma_gemm<H, BM, BN, WM, WN, false, true>), grid, block, 0, s, p);
+  // 16-byte staging needs both operands aligned with contiguous extents that are
+  // multiples of 8 elements (so chunks never straddle an edge).
+  const int64_t a_ext = p.a_col ? p.M : p.K, b_ext = p.b_col ? p.K : p.N;
+  const bool vec = p.vec_a && p.vec_b && a_ext % 8 == 0 && b_ext % 8 == 0;
+#define MHG_LAUNCH(AK, BKC, V) \
+  hipLaunchKernelGGL((mfma_gemm<H, BM, BN, WM, WN, AK, BKC, V>), grid, block, 0, s, p)
+  if (vec) {
+    if (!p.a_col && !p.b_col) MHG_LAUNCH(true, false, true);
+    else if (!p.a_col && p.b_col) MHG_LAUNCH(true, true, true);
+    else if (p.a_col && !p.b_col) MHG_LAUNCH(false, false, true);
+    else MHG_LAUNCH(false, true, true);
+  } else {
+    if (!p.a_col && !p.b_col) MHG_LAUNCH(true, false, false);
+    else if (!p.a_col && p.b_col) MHG_LAUNCH(true, true, false);
+    else if (p.a_col && !p.b_col) MHG_LAUNCH(false, false, false);
+    else MHG_LAUNCH(false, true, false);
+  }
+#undef MHG_LAUNCH
   return hipGetLastError();
 }
 

@@ -29,16 +29,27 @@ constexpr unsigned kHalf = (1u << E_F16) | (1u << E_BF16);
 
 // Registers per lane (VGPR + AGPR) each variant needs, from the compiler's
 // resource report of the gfx950 build; used for the occupancy limit.
+// Ring variants come before the register-staged variant of the same tile so that
+// they win ties; `fallback` names the register-staged variant run instead when the
+// operands' alignment rules a ring kernel out at run time (a LauncherId; -1: none).
 const Variant kCatalogue[] = {
-    // kind            bm   bn   bk  wm wn st sk   thr  types  launcher         tm tn
-    {{GEMM_KIND_FMA, 32, 32, 32, 4, 1, 2, 1}, 256, kF32, L_FMA_32, 2, 2},
-    {{GEMM_KIND_FMA, 64, 64, 16, 4, 1, 2, 1}, 256, kF32, L_FMA_64, 4, 4},
-    {{GEMM_KIND_FMA, 128, 128, 16, 4, 1, 2, 1}, 256, kF32, L_FMA_128, 8, 8},
-    {{GEMM_KIND_MFMA, 64, 64, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_64x64, 2, 2},
-    {{GEMM_KIND_MFMA, 128, 128, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_128x128, 4, 4},
-    {{GEMM_KIND_MFMA, 256, 128, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_256x128, 8, 4},
-    {{GEMM_KIND_MFMA, 256, 256, 64, 2, 4, 2, 1}, 512, kHalf, L_MFMA_256x256, 8, 4},
+    // kind            bm   bn   bk  wm wn st sk   thr  types  launcher           tm tn fallback
+    {{GEMM_KIND_FMA, 32, 32, 32, 4, 1, 2, 1}, 256, kF32, L_FMA_32, 2, 2, -1},
+    {{GEMM_KIND_FMA, 64, 64, 16, 4, 1, 2, 1}, 256, kF32, L_FMA_64, 4, 4, -1},
+    {{GEMM_KIND_FMA, 128, 128, 16, 4, 1, 2, 1}, 256, kF32, L_FMA_128, 8, 8, -1},
+    {{GEMM_KIND_MFMA, 64, 64, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_64x64, 2, 2, -1},
+    {{GEMM_KIND_MFMA, 128, 128, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_128x128_W4, 4, 4, L_MFMA_128x128},
+    {{GEMM_KIND_MFMA, 128, 128, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_128x128, 4, 4, -1},
+    {{GEMM_KIND_MFMA, 256, 128, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_256x128, 8, 4, -1},
+    {{GEMM_KIND_MFMA, 256, 256, 64, 2, 2, 2, 1}, 256, kHalf, L_BIG_256, 8, 8, L_MFMA_256x256},
+    {{GEMM_KIND_MFMA, 256, 256, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_256x256_W4, 8, 8, L_MFMA_256x256},
+    {{GEMM_KIND_MFMA, 256, 256, 32, 2, 4, 4, 1}, 512, kHalf, L_RING_256x256_W8, 8, 4, L_MFMA_256x256},
+    {{GEMM_KIND_MFMA, 256, 256, 64, 2, 4, 2, 1}, 512, kHalf, L_MFMA_256x256, 8, 4, -1},
 };
+
+bool is_ring(int launcher) {
+  return launcher == L_RING_256x256_W4 || launcher == L_RING_256x256_W8 || launcher == L_RING_128x128_W4;
+}
 
 // Largest tile intensity among the catalogue's tiles of an element size; the tile
 // reuse factor is measured against it.
@@ -53,6 +64,10 @@ double best_intensity(int elem, unsigned mask) {
 // registers.  FMA: TM*TN accumulators + TM + TN operands + staged elements.
 // MFMA: 4 fp32 per 16x16 block + fragments + staged 16-byte chunks.
 int regs_estimate(const Variant &v) {
+  if (v.launcher == L_BIG_256) return 512;   // one wave per SIMD: 256 accumulators in AGPRs
+  if (is_ring(v.launcher)) {   // accumulators + two fragment sets + addressing
+    return v.tm * v.tn * 4 + 2 * (v.tm + v.tn) * 4 + 24;
+  }
   const TileConfig &c = v.cfg;
   if (c.kind == GEMM_KIND_FMA) {
     int staged = (c.bm * c.bk + c.bk * c.bn) / v.threads;
@@ -69,6 +84,12 @@ int regs_estimate(const Variant &v) {
 const Variant *catalogue(int *count) {
   *count = static_cast<int>(sizeof(kCatalogue) / sizeof(kCatalogue[0]));
   return kCatalogue;
+}
+
+const Variant *variant_of_launcher(int launcher) {
+  for (const Variant &v : kCatalogue)
+    if (v.launcher == launcher) return &v;
+  return nullptr;
 }
 
 bool split_dtype(int dtype, int *in_code, int *out_code) {
@@ -168,8 +189,28 @@ bool validate(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t
   return true;
 }
 
+bool ring_shape_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bool a_col, bool b_col,
+                   int bm, int bn, int bk) {
+  const int64_t a_ext = a_col ? M : K, b_ext = b_col ? K : N;
+  if (a_ext % 8 || b_ext % 8 || lda % 8 || ldb % 8) return false;
+  const int64_t a_span = (a_col ? bk : bm) * lda * 2, b_span = (b_col ? bn : bk) * ldb * 2;
+  return a_span < (int64_t(1) << 31) && b_span < (int64_t(1) << 31);
+}
+
+bool needs_aligned_staging(int launcher) { return is_ring(launcher) || launcher == L_BIG_256; }
+
 double score(const Variant &v, const PlanData &p, const Hardware &hw, std::string *why) {
   const int elem = elem_bytes(p.in_code);
+  if (v.launcher == L_BIG_256 && (p.layout & GEMM_A_COL)) {
+    if (why) *why = "256x256 four-wave variant needs row-major A";
+    return -1.0;
+  }
+  if (needs_aligned_staging(v.launcher) &&
+      !ring_shape_ok(p.M, p.N, p.K, p.lda, p.ldb, p.layout & GEMM_A_COL, p.layout & GEMM_B_COL,
+                     v.cfg.bm, v.cfg.bn, v.cfg.bk)) {
+    if (why) *why = "variant with direct 16-byte staging needs extents and leading dimensions that are multiples of 8";
+    return -1.0;
+  }
   if (!(v.in_mask & (1u << p.in_code))) {
     if (why) *why = "variant does not take this input type";
     return -1.0;

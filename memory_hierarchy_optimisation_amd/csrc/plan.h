@@ -20,6 +20,10 @@ enum LauncherId {
   L_MFMA_128x128,
   L_MFMA_256x128,
   L_MFMA_256x256,
+  L_RING_256x256_W4,
+  L_RING_256x256_W8,
+  L_RING_128x128_W4,
+  L_BIG_256,
   L_SKINNY,
   L_COUNT
 };
@@ -40,7 +44,17 @@ struct Variant {
   unsigned in_mask;   // bit e set: input element code e supported
   int launcher;       // LauncherId
   int tm, tn;         // per-lane register tile (FMA) or per-wave 16x16 MFMA blocks (MFMA)
+  int fallback;       // LauncherId run instead when run-time checks rule this one out (-1: none)
 };
+
+// Ring variants (direct global-to-LDS loads) need 16-byte aligned operands whose
+// contiguous extents and leading dimensions are multiples of 8 elements, and slab
+// offsets below 2^31 bytes.
+bool ring_shape_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bool a_col, bool b_col,
+                   int bm, int bn, int bk);
+// Variants with a fallback need direct 16-byte staging; the plan checks what it can see
+// (extents and leading dimensions), gemm_run checks pointer alignment.
+bool needs_aligned_staging(int launcher);
 
 // Hardware description used by the resource model.
 struct Hardware {
@@ -62,6 +76,7 @@ struct LaunchArgs {
   int out_code;    // Elem
   int a_col, b_col;
   int vec_a, vec_b;   // 1: 16-byte loads allowed (aligned base and leading dimension)
+  int c_vec;          // 1: C's base and leading dimension allow 4-element vector stores
   int gm, gn;         // tiles along M and N
   int split_k;
   int group_m;        // rows of tiles walked together (L2 locality)
@@ -85,6 +100,7 @@ struct PlanData {
 
 // Catalogue of compiled variants.
 const Variant *catalogue(int *count);
+const Variant *variant_of_launcher(int launcher);
 
 // Input / output element codes of a gemm_dtype, or false when unknown.
 bool split_dtype(int dtype, int *in_code, int *out_code);

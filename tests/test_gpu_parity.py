@@ -33,7 +33,8 @@ def _catalogue_for(in_t):
     if in_t == "f32":
         return [(1, 32, 32, 32, 4, 1, 2, 1), (1, 64, 64, 16, 4, 1, 2, 1), (1, 128, 128, 16, 4, 1, 2, 1)]
     return [(2, 64, 64, 64, 2, 2, 2, 1), (2, 128, 128, 64, 2, 2, 2, 1), (2, 256, 128, 64, 2, 2, 2, 1),
-            (2, 256, 256, 64, 2, 4, 2, 1)]
+            (2, 256, 256, 64, 2, 4, 2, 1), (2, 128, 128, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 2, 4, 1),
+            (2, 256, 256, 32, 2, 4, 4, 1), (2, 256, 256, 64, 2, 2, 2, 1)]
 
 
 # ---- the measured workloads at full size ---------------------------------------------------
@@ -112,16 +113,46 @@ def test_ragged_extents(in_t, out_t):
             check_tolerance(C, Cref, out_t, f"M={M} N={N} K={K} a_col={a_col} b_col={b_col}")
 
 
+ALIGNED_ONLY = {(2, 128, 128, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 4, 4, 1),
+                (2, 256, 256, 64, 2, 2, 2, 1)}
+ROW_MAJOR_A_ONLY = {(2, 256, 256, 64, 2, 2, 2, 1)}
+
+
 @pytest.mark.parametrize("in_t,out_t", ALL_DTYPES)
 def test_every_variant_every_layout_ragged(in_t, out_t):
-    M, N, K = 300, 270, 200
+    """Every compiled variant forced on a shape that leaves partial tiles and a partial
+    K slab; the variants with direct 16-byte staging get extents that are multiples of 8."""
     for cfg in _catalogue_for(in_t):
+        M, N, K = (304, 272, 200) if cfg in ALIGNED_ONLY else (300, 270, 200)
         for a_col, b_col in LAYOUTS:
             As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, seed=3)
+            if a_col and cfg in ROW_MAJOR_A_ONLY:
+                with pytest.raises(mh.GemmError, match="row-major A"):
+                    run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, cfg=cfg)
+                continue
             C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, cfg=cfg)
             assert (desc["bm"], desc["bn"]) == (cfg[1], cfg[2])
             Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
             check_tolerance(C, Cref, out_t, f"cfg={cfg} a_col={a_col} b_col={b_col}")
+
+
+def test_aligned_variants_refuse_extents_that_are_not_multiples_of_8():
+    for cfg in ALIGNED_ONLY:
+        As, lda, Bs, ldb, _, _ = synth.operands(300, 270, 200, "bf16", seed=3)
+        with pytest.raises(mh.GemmError, match="multiples of 8"):
+            run_gpu(As, lda, Bs, ldb, 300, 270, 200, "bf16", "bf16", cfg=cfg)
+
+
+@pytest.mark.parametrize("cfg", sorted(ALIGNED_ONLY))
+@pytest.mark.parametrize("b_col", [False, True])
+def test_aligned_variants_fall_back_on_misaligned_pointers(cfg, b_col):
+    """Run-time fallback to the register-staged kernel when a base pointer is not
+    16-byte aligned: same plan, still correct."""
+    M, N, K = 264, 520, 136
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "bf16", False, b_col, seed=6)
+    C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "bf16", "f32", False, b_col, cfg=cfg,
+                           offset_a=1, offset_b=0)
+    check_tolerance(C, oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16", False, b_col), "f32")
 
 
 @pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
