@@ -23,15 +23,17 @@
 // staged: each lane loads an 8 x 8 block (8 k-rows of 8 n-values) and repacks it into
 // 8 n-rows of 8 k-values before the LDS store.
 //
-// Pipeline per 64-deep slab t (LDS double buffer, register-staged global loads):
-//   read fragments of k-step 1        | matrix instructions of k-step 0
-//   store slab t+1 (loaded during t-1) to the other LDS buffer; load slab t+2
-//   first half of k-step 1's matrix instructions
-//   wait for this wave's LDS operations; barrier
-//   read fragments of slab t+1, k-step 0 | second half of k-step 1
-// so the LDS reads after the barrier overlap matrix instructions.  The barrier is an
-// s_barrier after an explicit LDS wait: the C++ block barrier would also wait for the
-// global loads of slab t+2, which are meant to stay in flight across it.
+// Staging keeps two slabs in flight in the 160 KB of LDS:
+//   * A slabs are loaded straight into LDS (buffer loads with an LDS destination, the
+//     gfx950 counterpart of the asynchronous global-to-shared copy of "Tiling 策略与
+//     内存层次优化", cp.async section) into a ring of three 32 KiB slots;
+//   * B slabs go through two register sets (each loaded two slabs ahead), are
+//     transposed there if B is row-major, and are stored into two 32 KiB LDS slots.
+// Each 64-deep slab runs 64 matrix instructions in four groups of 16; between them the
+// wave issues the B stores and loads, the A loads, and the LDS reads of the next
+// fragments, interleaved instruction by instruction (scheduling-group barriers).  One
+// block barrier per slab, issued as s_barrier after an explicit wait that leaves the
+// younger loads in flight (the C++ block barrier would wait for all of them).
 //
 // Edges: loads outside the matrix read zeros through buffer-resource range checks
 // ("CUDA tile", 4: zero is the identity of the sum); stores are masked.  The kernel
@@ -46,108 +48,369 @@ namespace big {
 
 constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
 constexpr int WTM = 128, WTN = 128;
-constexpr int FM = 8, FN = 8;   // operand fragments per 32-deep k-step: 4 row blocks x 2 k-halves
 constexpr int TILE_BYTES = 256 * BK * 2;      // one operand's slab: 32 KiB
-constexpr int STAGE = 2 * TILE_BYTES;          // A and B
 constexpr uint32_t kOut = 0x80000000u;         // beyond every buffer range: loads zeros
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
-// Byte offset of 16-byte chunk c (0..7) of row r in a K-contiguous 256 x 64 tile.
-// Eight consecutive rows read at one chunk column land on eight distinct bank groups.
-__device__ __forceinline__ int koff(int r, int c) { return r * 128 + ((c ^ (r & 7)) << 4); }
+// Byte offset of 16-byte chunk c (0..7) of row r in a K-contiguous 256 x 64 tile (128
+// bytes a row).  The LDS serves a 16-byte-per-lane access 16 lanes at a time from 64
+// four-byte banks, i.e. 16 distinct 16-byte slots (address / 16 mod 16) per cycle.
+// Row r starts at slot 8 (r % 2); XOR-ing the chunk with (r / 2) % 8 makes the 16
+// rows r0 .. r0 + 15 (r0 even) read at one chunk column land on 16 distinct slots.
+__device__ __forceinline__ int koff(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
 
-__device__ __forceinline__ void lds_wait_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// LDS accesses through 32-bit LDS addresses, so that every per-lane address is one
+// register plus a constant the instruction's 16-bit offset field absorbs.
+__device__ __forceinline__ u32x4 lds_ld(uint32_t a) {
+  return *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(a));
+}
+__device__ __forceinline__ void lds_st(uint32_t a, u32x4 v) {
+  *reinterpret_cast<MHG_LDS u32x4 *>(size_t(a)) = v;
+}
+// A copy of x the compiler cannot see through.  Taken once per slab, it keeps the
+// per-slab address arithmetic (one XOR or add each) inside the loop instead of
+// letting it be hoisted into dozens of loop-invariant registers.
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
-// Instruction-group masks of the scheduling barriers.
-constexpr int kMfma = 0x008, kVmemRead = 0x020, kDsRead = 0x100, kDsWrite = 0x200, kValu = 0x002;
-
-// Interleave the preceding region: n rounds of (1 matrix instruction, k LDS reads).
-template <int n, int k>
-__device__ __forceinline__ void interleave_mfma_dsread() {
-#pragma unroll
-  for (int i = 0; i < n; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kDsRead, k, 0);
+// Row-major B (N-contiguous in memory): lane t owns the 8 x 8 block of k-rows
+// 8*(t % 8) .. +7 and n-columns 8*(t / 8) .. +7 of the slab.  Load i reads k-row
+// 8*(t%8) + i; eight neighbouring lanes read eight k-rows, and the eight lane groups of
+// a wave read 128 contiguous bytes of each.  The block is transposed in registers and
+// stored as 8 n-rows of 8 k-values: n-row 8*(t/8) + j, k-chunk t % 8.
+struct GeoBn {
+  uint32_t off;        // byte offset of k-row 8*(t%8), n-chunk t/8
+  uint32_t stride;     // one k-row, in bytes
+  int klim;            // k-rows of the matrix at and below 8*(t%8); very negative if the
+                       // lane's columns lie past N
+  uint32_t st_base;    // see store_one
+  uint32_t sel[2];     // byte selectors of store_one for even and odd j
+  __device__ __forceinline__ void init(int64_t ldb, int n0, int64_t N, int64_t K) {
+    const int kg = threadIdx.x % 8, nc = threadIdx.x / 8, par = nc & 1;
+    off = uint32_t((int64_t(8 * kg) * ldb + 8 * nc) * 2);
+    stride = uint32_t(ldb * 2);
+    klim = n0 + 8 * nc < N ? int(min<int64_t>(K - 8 * kg, 1 << 30)) : -(1 << 30);
+    st_base = uint32_t(1024 * nc) | uint32_t(128 * par) | uint32_t((kg ^ (4 * par)) << 4);
+    // low halves of both words for an even n-row, high halves for an odd one
+    sel[0] = par ? 0x07060302u : 0x05040100u;
+    sel[1] = par ? 0x05040100u : 0x07060302u;
   }
-}
-
-// Staging of the A slab (row-major: K-contiguous): 2048 chunks, 8 per lane.
-// Chunk q = lane_id + 256 i: row q / 8, k-chunk q % 8.
-// Load i reads row threadIdx.x / 8 + 32 i: one per-lane byte offset plus a uniform
-// stride of 32 rows, passed as the load's scalar offset.
-struct StageA {
-  u32x4 r[8];
-  uint32_t off;        // byte offset of row threadIdx.x / 8, chunk threadIdx.x % 8
-  uint32_t stride;     // 32 rows, in bytes
-  int rows_left;       // rows of the matrix at and below this lane's first row
-  __device__ __forceinline__ void init(int64_t lda, int m0, int64_t M) {
-    off = uint32_t((int64_t(threadIdx.x / 8) * lda + 8 * (threadIdx.x % 8)) * 2);
-    stride = uint32_t(32 * lda * 2);
-    rows_left = int(min<int64_t>(M - m0 - int64_t(threadIdx.x / 8), 1 << 30));
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *B, int64_t ldb, int n0, int k0) const {
+    return rsrc_of(B + int64_t(k0) * ldb + n0);
   }
-  __device__ __forceinline__ void load(const uint16_t *A, int64_t lda, int m0, int k0, int64_t K) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc_of(A + int64_t(m0) * lda + k0);
-    const bool k_in = k0 + 8 * int(threadIdx.x % 8) < K;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool in = k_in && 32 * i < rows_left;
-      r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? off : kOut, int(i * stride), 0);
-    }
+  __device__ __forceinline__ u32x4 load_one(__amdgpu_buffer_rsrc_t rs, int k0, int i) const {
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, i < klim - k0 ? off : kOut, int(i * stride), 0);
   }
-  __device__ __forceinline__ void store(char *tile) const {
+  // Store j writes n-row jj = j ^ (n-chunk parity) of the lane's block, so that the 16
+  // lanes of an LDS cycle (two n-chunks) cover rows of both parities and 16 distinct
+  // slots.  Its offset koff(8 nc + jj, kg) = 1024 nc + 128 jj + 16 (kg ^ 4 (nc % 2)
+  // ^ j / 2) is st_base ^ (128 j + 16 (j / 2)); `base` is st_base.  jj and j share the
+  // register word j / 2; the half is picked per lane by the selector.
+  __device__ __forceinline__ void store_one(const u32x4 (&r)[8], uint32_t base, uint32_t tile, int j) const {
+    const uint32_t s = sel[j & 1];
+    const int w = j >> 1;
+    u32x4 v;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = threadIdx.x + NT * i;
-      *reinterpret_cast<u32x4 *>(tile + koff(q / 8, q % 8)) = r[i];
-    }
+    for (int e = 0; e < 4; ++e)   // k = 8 (t%8) + 2e (low half) and 8 (t%8) + 2e + 1 (high half)
+      v[e] = __builtin_amdgcn_perm(r[2 * e + 1][w], r[2 * e][w], s);
+    lds_st((base ^ uint32_t(128 * j + 16 * (j >> 1))) + tile, v);
   }
 };
 
-// Staging of a column-major B slab (K-contiguous): same shape as A with n for m.
-using StageBk = StageA;
-
-// Staging of a row-major B slab (N-contiguous): lane t owns the 8 x 8 block of k-rows
-// 8*(t % 8) .. +7 and n-columns 8*(t / 8) .. +7.  Load i reads k-row 8*(t%8) + i; eight
-// neighbouring lanes read eight k-rows, and the eight lane-groups of a wave read 128
-// contiguous bytes of each.
-struct StageBn {
-  u32x4 r[8];
-  uint32_t off;        // byte offset of k-row 8*(t%8), n-chunk t/8
-  uint32_t stride;     // one k-row, in bytes
-  bool col_ok;
-  __device__ __forceinline__ void init(int64_t ldb, int n0, int64_t N) {
-    const int kg = threadIdx.x % 8, nc = threadIdx.x / 8;
-    off = uint32_t((int64_t(8 * kg) * ldb + 8 * nc) * 2);
-    stride = uint32_t(ldb * 2);
-    col_ok = n0 + 8 * nc < N;
+// Column-major B (K-contiguous): 2048 16-byte chunks, 8 per lane; chunk
+// t + 256 i is n-row t / 8 + 32 i, k-chunk t % 8, stored unchanged.
+struct GeoBk {
+  uint32_t off;        // byte offset of n-row t / 8, k-chunk t % 8
+  uint32_t stride;     // 32 n-rows, in bytes
+  int rows_left;       // n-rows of the matrix at and below the lane's first
+  int klim;            // slabs with k0 < klim have the lane's chunk inside K
+  uint32_t st_base;    // koff(t / 8, t % 8)
+  __device__ __forceinline__ void init(int64_t ldb, int n0, int64_t N, int64_t K) {
+    const int row = threadIdx.x / 8, c = threadIdx.x % 8;
+    off = uint32_t((int64_t(row) * ldb + 8 * c) * 2);
+    stride = uint32_t(32 * ldb * 2);
+    rows_left = int(min<int64_t>(N - n0 - row, 1 << 30));
+    klim = int(min<int64_t>(K - 8 * c, 1 << 30));
+    st_base = uint32_t(koff(row, c));
   }
-  __device__ __forceinline__ void load(const uint16_t *B, int64_t ldb, int n0, int k0, int64_t K) {
-    const __amdgpu_buffer_rsrc_t rs = rsrc_of(B + int64_t(k0) * ldb + n0);
-    const int kleft = int(min<int64_t>(K - k0 - 8 * int(threadIdx.x % 8), 1 << 30));
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *B, int64_t ldb, int n0, int k0) const {
+    return rsrc_of(B + int64_t(n0) * ldb + k0);
+  }
+  __device__ __forceinline__ u32x4 load_one(__amdgpu_buffer_rsrc_t rs, int k0, int i) const {
+    const int lim = k0 < klim ? rows_left : 0;
+    return __builtin_amdgcn_raw_buffer_load_b128(rs, 32 * i < lim ? off : kOut, int(i * stride), 0);
+  }
+  __device__ __forceinline__ void store_one(const u32x4 (&r)[8], uint32_t base, uint32_t tile, int i) const {
+    lds_st(base + tile + 4096 * i, r[i]);
+  }
+};
+
+// A's slab (K-contiguous) loaded straight into LDS.  A load instruction of a wave
+// fills 64 consecutive 16-byte slots: load j of wave w covers rows 32 j + 8 w .. +7,
+// lane l the row 32 j + 8 w + l / 8 and LDS slot l % 8 of it, which holds the row's
+// k-chunk (l % 8) ^ ((row / 2) % 8) -- the XOR swizzle of koff applied on the global side.
+struct DmaA {
+  uint32_t off;        // byte offset of this lane's chunk for j = 0, from the slab origin
+  uint32_t stride;     // 32 rows, in bytes
+  int rows_left;       // rows of the matrix at and below this lane's first row
+  int klim;            // slabs with k0 < klim have this lane's chunk inside K
+  __device__ __forceinline__ void init(int64_t lda, int m0, int64_t M, int64_t K) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int row = 8 * wave + lane / 8, c = (lane % 8) ^ ((row >> 1) & 7);
+    off = uint32_t((int64_t(row) * lda + 8 * c) * 2);
+    stride = uint32_t(32 * lda * 2);
+    rows_left = int(min<int64_t>(M - m0 - row, 1 << 30));
+    klim = int(min<int64_t>(K - 8 * c, 1 << 30));
+  }
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *A, int64_t lda, int m0, int k0) const {
+    return rsrc_of(A + int64_t(m0) * lda + k0);
+  }
+  // Rows of the slab at k0 this lane may load: 0 when its chunk lies past K.
+  __device__ __forceinline__ int lim(int k0) const { return k0 < klim ? rows_left : 0; }
+  // Load j of the slab (resource rs, row limit l) into the LDS tile at `dst`.  `dst`
+  // and `wave` are wave-uniform: the LDS destination of these loads is a scalar register.
+  __device__ __forceinline__ void issue_one(__amdgpu_buffer_rsrc_t rs, int l, uint32_t dst, uint32_t wave,
+                                            int j) const {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MHG_LDS void *)(size_t)(dst + (4 * j + wave) * 1024), 16,
+                                             32 * j < l ? off : kOut, int(j * stride), 0, 0);
+  }
+  __device__ __forceinline__ void issue(const uint16_t *A, int64_t lda, int m0, int k0, uint32_t dst,
+                                        uint32_t wave) const {
+    const __amdgpu_buffer_rsrc_t rs = rsrc(A, lda, m0, k0);
+    const int l = lim(k0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool in = col_ok && i < kleft;
-      r[i] = __builtin_amdgcn_raw_buffer_load_b128(rs, in ? off : kOut, int(i * stride), 0);
+    for (int j = 0; j < 8; ++j) issue_one(rs, l, dst, wave, j);
+  }
+};
+
+// s_waitcnt with vmcnt = n and lgkmcnt = 0 (expcnt free), then the block barrier.
+template <int n>
+__device__ __forceinline__ void wait_vm_lgkm_barrier() {
+  static_assert(n >= 0 && n < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4));
+  asm volatile("s_barrier" ::: "memory");
+}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (3 << 14)); }
+// Nothing moves across it: the instruction order of a phase is the source order.
+#define MHG_ORDER() __builtin_amdgcn_sched_barrier(0)
+
+// LDS map: B slabs in slots 0 and 1 (slab s in slot s % 2), the A ring in slots 2..4
+// (slab s in slot 2 + s % 3); a slot is one 256 x 64 K-contiguous tile (32 KiB).  B's
+// slots come first so that their offsets fit the LDS instructions' offset field.
+template <class H, bool B_KC>
+struct BigGemm {
+  using GeoB = typename std::conditional<B_KC, GeoBk, GeoBn>::type;
+  const LaunchArgs &p;
+  const uint16_t *A, *B;
+  int m0, n0, KT;
+  uint32_t lds0;                 // LDS address of slot 0
+  uint32_t wave;                 // wave index, wave-uniform
+  uint32_t fa_base, fb_base;     // koff of the lane's fragment rows for k-half 0
+  DmaA da;
+  GeoB gb;
+  u32x4 rb[2][8];                // B register sets: slab s is staged in set s % 2
+  f32x16 acc[4][4];
+  // Fragments of one k-half (16 deep): 4 row blocks of A, 4 column blocks of B.  Phase
+  // p of a slab multiplies the half in set p % 2 while the next half is read into the
+  // other set, so 64 registers hold all fragments.
+  u32x4 fa[2][4], fb[2][4];
+
+  __device__ __forceinline__ BigGemm(const LaunchArgs &p_) : p(p_) {}
+
+  __device__ __forceinline__ uint32_t a_slot(int slab) const { return lds0 + (2 + slab % 3) * TILE_BYTES; }
+
+  // Fragment of row block i, k-half q (q = 0..3 over the slab): the lane reads row
+  // (lane % 32) of the block and k-chunk 2 q + lane / 32, i.e. koff(row, chunk) =
+  // base ^ (32 q) + 4096 i with base = koff(row, lane / 32).
+  template <int SET>
+  __device__ __forceinline__ void read_half(uint32_t ab, uint32_t bb, uint32_t ta, uint32_t tb, int q) {
+    const uint32_t xa = (ab ^ uint32_t(q << 5)) + ta, xb = (bb ^ uint32_t(q << 5)) + tb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[SET][i] = lds_ld(xa + 4096 * i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) fb[SET][j] = lds_ld(xb + 4096 * j);
+  }
+  template <int SET>
+  __device__ __forceinline__ void load_b(int k0) {
+    const __amdgpu_buffer_rsrc_t rs = gb.rsrc(B, p.ldb, n0, k0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rb[SET][i] = gb.load_one(rs, k0, i);
+  }
+  template <int SET>
+  __device__ __forceinline__ void store_b(uint32_t base, uint32_t tile) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) gb.store_one(rb[SET], base, tile, j);
+  }
+
+  // Matrix instruction n (0..15) of a k-half: accumulator (n / 4, n % 4).
+  template <int SET>
+  __device__ __forceinline__ void mma(int n) {
+    const int i = n >> 2, j = n & 3;
+    acc[i][j] = mfma32(H{}, fb[SET][j], fa[SET][i], acc[i][j]);
+  }
+  // LDS read n (0..7) of a k-half: A row block n for n < 4, else B column block n - 4;
+  // xa, xb are the half's lane offsets (half_off).
+  template <int SET>
+  __device__ __forceinline__ void read_one(uint32_t xa, uint32_t xb, int n) {
+    if (n < 4) fa[SET][n] = lds_ld(xa + 4096 * n);
+    else fb[SET][n - 4] = lds_ld(xb + 4096 * (n - 4));
+  }
+  __device__ __forceinline__ static uint32_t half_off(uint32_t base, int q, uint32_t tile) {
+    return (base ^ uint32_t(q << 5)) + tile;
+  }
+
+  // One 64-deep slab t: four phases of 16 matrix instructions, each multiplying the
+  // k-half in fragment set p % 2 while the next half is read into the other set, with
+  // one global or LDS operation after every other matrix instruction.  The order inside
+  // a phase is fixed (MHG_ORDER between steps) so that the matrix pipe never waits
+  // behind a burst of memory instructions.  Every phase starts by waiting for the LDS
+  // operations of the previous one (issued a whole phase earlier): the LDS counter
+  // saturates at 15, and without that wait a fragment consumed late in a phase would
+  // also wait for the reads and writes issued early in it.
+  //
+  // BS = (t + 1) % 2.  On entry: fragment set 0 holds k-half 0 of slab t; A slab t is
+  // in LDS and A slab t+1 in flight; B slab t is in LDS, B slab t+1 in register set BS
+  // and slab t+2 in set 1 - BS (loads possibly in flight).
+  template <int BS>
+  __device__ __forceinline__ void slab(int t) {
+    const uint32_t ab = opaque(fa_base), bb = opaque(fb_base), sbase = opaque(gb.st_base);
+    const uint32_t ca = a_slot(t), cb = lds0 + (1 - BS) * TILE_BYTES, nb = lds0 + BS * TILE_BYTES;
+    // Phase 0: B slab t+1 out of register set BS into its LDS slot (slab t-1's, whose
+    // readers all passed the previous barrier).
+    wait_lgkm0();
+    MHG_ORDER();
+    {
+      const uint32_t xa = half_off(ab, 1, ca), xb = half_off(bb, 1, cb);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        mma<0>(2 * k); MHG_ORDER();
+        read_one<1>(xa, xb, k); MHG_ORDER();
+        mma<0>(2 * k + 1); MHG_ORDER();
+        gb.store_one(rb[BS], sbase, nb, k); MHG_ORDER();
+      }
+    }
+    // Phase 1: A slab t+2 requested into the ring slot slab t-1 used.
+    wait_lgkm0();
+    MHG_ORDER();
+    {
+      const uint32_t xa = half_off(ab, 2, ca), xb = half_off(bb, 2, cb);
+      const int k0 = (t + 2) * BK;
+      const __amdgpu_buffer_rsrc_t rs = da.rsrc(A, p.lda, m0, k0);
+      const int l = da.lim(k0);
+      const uint32_t dst = a_slot(t + 2);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        mma<1>(2 * k); MHG_ORDER();
+        read_one<0>(xa, xb, k); MHG_ORDER();
+        mma<1>(2 * k + 1); MHG_ORDER();
+        da.issue_one(rs, l, dst, wave, k); MHG_ORDER();
+      }
+    }
+    // Phase 2: register set BS refilled with B slab t+3.
+    wait_lgkm0();
+    MHG_ORDER();
+    {
+      const uint32_t xa = half_off(ab, 3, ca), xb = half_off(bb, 3, cb);
+      const int k0 = (t + 3) * BK;
+      const __amdgpu_buffer_rsrc_t rs = gb.rsrc(B, p.ldb, n0, k0);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        mma<0>(2 * k); MHG_ORDER();
+        read_one<1>(xa, xb, k); MHG_ORDER();
+        mma<0>(2 * k + 1); MHG_ORDER();
+        rb[BS][k] = gb.load_one(rs, k0, k); MHG_ORDER();
+      }
+    }
+    // A slab t+1 landed: the loads issued after its last one are slab t-1's 8 B loads
+    // and this slab's 8 A and 8 B loads.  Every wave stored B slab t+1 and finished
+    // reading slab t.
+    wait_vm_lgkm_barrier<24>();
+    MHG_ORDER();
+    // Phase 3: k-half 0 of slab t+1 read.
+    {
+      const uint32_t xa = half_off(ab, 0, a_slot(t + 1)), xb = half_off(bb, 0, nb);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        mma<1>(2 * k); MHG_ORDER();
+        read_one<0>(xa, xb, k); MHG_ORDER();
+        mma<1>(2 * k + 1); MHG_ORDER();
+      }
     }
   }
-  // Transpose the 8 x 8 block of 16-bit values and store n-row by n-row.
-  __device__ __forceinline__ void store(char *tile) const {
-    const int kg = threadIdx.x % 8, nc = threadIdx.x / 8;
+
+  __device__ __forceinline__ void run(uint32_t lds_base) {
+    int tm, tn;
+    tile_of(blockIdx.x, p.gm, p.gn, p.group_m, tm, tn);
+    m0 = tm * BM;
+    n0 = tn * BN;
+    lds0 = lds_base;
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    fa_base = uint32_t(koff(wm * WTM + (lane & 31), lane >> 5));
+    fb_base = uint32_t(koff(wn * WTN + (lane & 31), lane >> 5));
+    A = static_cast<const uint16_t *>(p.A);
+    B = static_cast<const uint16_t *>(p.B);
+    const int64_t K = p.K;
+    KT = int((K + BK - 1) / BK);
+    da.init(p.lda, m0, p.M, K);
+    gb.init(p.ldb, n0, p.N, K);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {        // n = 8*nc + j
-      // byte selector: low halves of both words for even j, high halves for odd j
-      const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-      const int w = j >> 1;
-      u32x4 v;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)   // k = 8kg + 2e (low half) and 8kg + 2e + 1 (high half)
-        v[e] = __builtin_amdgcn_perm(r[2 * e + 1][w], r[2 * e][w], sel);
-      *reinterpret_cast<u32x4 *>(tile + koff(8 * nc + j, kg)) = v;
+      for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    // Prologue: B slab 0 through set 0 into slot 0, A slabs 0 and 1 requested, B slabs
+    // 1 and 2 into sets 1 and 0.  Past K every load reads zeros, so the loop body has
+    // no branches and issues the same loads in every slab.
+    load_b<0>(0);
+    da.issue(A, p.lda, m0, 0, a_slot(0), wave);
+    wait_vm0();
+    store_b<0>(gb.st_base, lds0);
+    load_b<1>(BK);
+    da.issue(A, p.lda, m0, BK, a_slot(1), wave);
+    load_b<0>(2 * BK);
+    wait_vm_lgkm_barrier<24>();    // A slab 0 came before the wait above
+    read_half<0>(fa_base, fb_base, a_slot(0), lds0, 0);
+
+    // Two slabs per trip (register-set and LDS-slot indices are compile-time), the odd
+    // one out peeled: a conditional second slab inside the loop would merge two copies
+    // of the 256 accumulators at its end, which the register allocator resolves with
+    // spills.
+    int t = 0;
+    for (; t + 1 < KT; t += 2) {
+      slab<1>(t);
+      slab<0>(t + 1);
+    }
+    if (t < KT) slab<1>(t);
+    // Loads still in flight write LDS: drain them before the workgroup ends.
+    wait_vm0();
+
+    // acc[i][j] holds the transposed 32 x 32 block: element r of lane l is
+    // C[row m0 + 128 wm + 32 i + l % 32][col n0 + 128 wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4].
+    const int64_t row0 = m0 + wm * WTM + (lane & 31);
+    const int64_t colL = n0 + wn * WTN + 4 * (lane >> 5);
+    const bool c_vec = p.c_vec != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = row0 + 32 * i;
+      if (row >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = colL + 32 * j + 8 * q;
+          const int64_t n_in = p.N - col;
+          if (n_in <= 0) continue;
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          store_out4(p.C, row * p.ldc + col, v, p.out_code, c_vec && n_in >= 4, int(n_in));
+        }
     }
   }
 };
@@ -155,128 +418,9 @@ struct StageBn {
 template <class H, bool B_KC>
 __global__ void __launch_bounds__(NT)
 big_gemm(LaunchArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-  using StageB = typename std::conditional<B_KC, StageBk, StageBn>::type;
-
-  int tm, tn;
-  tile_of(blockIdx.x, p.gm, p.gn, p.group_m, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const uint16_t *A = static_cast<const uint16_t *>(p.A);
-  const uint16_t *B = static_cast<const uint16_t *>(p.B);
-  const int64_t K = p.K;
-
-  StageA sa;
-  StageB sb;
-  sa.init(p.lda, m0, p.M);
-  sb.init(p.ldb, n0, p.N);
-
-  // Fragment f of k-step s (k = 32 s .. 32 s + 31): row block f / 2 (32 rows), k-half
-  // f % 2; lane reads row (lane % 32) of the block, k-chunk 4 s + 2 (f % 2) + lane / 32.
-  const int arow = wm * WTM + (lane & 31), brow = wn * WTN + (lane & 31);
-  auto fragA = [&](const char *tile, int f, int s) {
-    const int r = arow + 32 * (f >> 1);
-    return *reinterpret_cast<const u32x4 *>(tile + koff(r, 4 * s + 2 * (f & 1) + (lane >> 5)));
-  };
-  auto fragB = [&](const char *tile, int f, int s) {
-    const int r = brow + 32 * (f >> 1);
-    return *reinterpret_cast<const u32x4 *>(tile + koff(r, 4 * s + 2 * (f & 1) + (lane >> 5)));
-  };
-  // acc[i][j] += A block i x B block j over k-half h of a 32-deep k-step, for the
-  // blocks i in [i0, i1).  Consecutive matrix instructions update different
-  // accumulators; the two k-halves of one accumulator are a whole half-step apart.
-  auto half = [&](f32x16 (&acc)[4][4], const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], int h, int i0, int i1) {
-#pragma unroll
-    for (int i = i0; i < i1; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma32(H{}, fb[2 * j + h], fa[2 * i + h], acc[i][j]);
-  };
-
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-  const int KT = int((K + BK - 1) / BK);
-  sa.load(A, p.lda, m0, 0, K);
-  sb.load(B, p.ldb, n0, 0, K);
-  sa.store(smem);
-  sb.store(smem + TILE_BYTES);
-  sa.load(A, p.lda, m0, BK, K);       // past K these read zeros: the loop body is
-  sb.load(B, p.ldb, n0, BK, K);       // branch-free so its phases can be interleaved
-  lds_wait_barrier();
-
-  u32x4 a0[FM], b0[FN], a1[FM], b1[FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) a0[i] = fragA(smem, i, 0);
-#pragma unroll
-  for (int j = 0; j < FN; ++j) b0[j] = fragB(smem + TILE_BYTES, j, 0);
-
-  for (int t = 0; t < KT; ++t) {
-    const char *cur = smem + (t & 1) * STAGE;
-    char *nxt = smem + ((t + 1) & 1) * STAGE;
-    // Phase 1: k-step 0 (32 matrix instructions), interleaved one-for-one with the
-    // 16 LDS reads of k-step 1's fragments.
-#pragma unroll
-    for (int j = 0; j < FN; ++j) b1[j] = fragB(cur + TILE_BYTES, j, 1);
-    half(acc, a0, b0, 0, 0, 4);
-#pragma unroll
-    for (int i = 0; i < FM; ++i) a1[i] = fragA(cur, i, 1);
-    half(acc, a0, b0, 1, 0, 4);
-    interleave_mfma_dsread<16, 1>();
-    __builtin_amdgcn_sched_barrier(0);
-    // Phase 2: first half of k-step 1 (16 matrix instructions) with slab t+1's LDS
-    // stores and slab t+2's global loads between them.
-    // (On the last slabs these store and load zeros into a buffer nobody reads.)
-    sa.store(nxt);
-    sb.store(nxt + TILE_BYTES);
-    sa.load(A, p.lda, m0, (t + 2) * BK, K);
-    sb.load(B, p.ldb, n0, (t + 2) * BK, K);
-    half(acc, a1, b1, 0, 0, 2);
-    half(acc, a1, b1, 1, 0, 2);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kDsWrite, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kValu, 2, 0);
-      __builtin_amdgcn_sched_group_barrier(kVmemRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    lds_wait_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    // Phase 3: second half of k-step 1 with the LDS reads of slab t+1's k-step 0.
-#pragma unroll
-    for (int i = 0; i < FM; ++i) a0[i] = fragA(nxt, i, 0);
-#pragma unroll
-    for (int j = 0; j < FN; ++j) b0[j] = fragB(nxt + TILE_BYTES, j, 0);
-    half(acc, a1, b1, 0, 2, 4);
-    half(acc, a1, b1, 1, 2, 4);
-    interleave_mfma_dsread<16, 1>();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-
-  // acc[i][j] holds the transposed 32 x 32 block: element r of lane l is
-  // C[row m0 + 128 wm + 32 i + l % 32][col n0 + 128 wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4].
-  const int64_t row0 = m0 + wm * WTM + (lane & 31);
-  const int64_t colL = n0 + wn * WTN + 4 * (lane >> 5);
-  const bool c_vec = p.c_vec != 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t row = row0 + 32 * i;
-    if (row >= p.M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = colL + 32 * j + 8 * q;
-        const int64_t n_in = p.N - col;
-        if (n_in <= 0) continue;
-        const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-        store_out4(p.C, row * p.ldc + col, v, p.out_code, c_vec && n_in >= 4, int(n_in));
-      }
-  }
+  __shared__ __attribute__((aligned(1024))) char smem[5 * TILE_BYTES];
+  BigGemm<H, B_KC> g(p);
+  g.run(uint32_t(size_t((MHG_LDS char *)smem)));
 }
 
 template __global__ void big_gemm<HalfBF16, false>(LaunchArgs);

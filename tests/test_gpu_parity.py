@@ -155,6 +155,23 @@ def test_aligned_variants_fall_back_on_misaligned_pointers(cfg, b_col):
     check_tolerance(C, oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16", False, b_col), "f32")
 
 
+BIG_256 = (2, 256, 256, 64, 2, 2, 2, 1)
+
+
+@pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("b_col", [False, True])
+def test_four_wave_256_kernel_every_slab_count(in_t, out_t, b_col):
+    """The 256 x 256 four-wave kernel pipelines two 64-deep slabs per loop trip and
+    peels an odd last slab; K from one partial slab to five slabs, on a ragged grid."""
+    M, N = 264, 520
+    for K in (8, 64, 72, 136, 200, 320):
+        As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, False, b_col, seed=K)
+        C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, False, b_col, cfg=BIG_256)
+        assert (desc["bm"], desc["bn"]) == (256, 256)
+        Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, False, b_col)
+        check_tolerance(C, Cref, out_t, f"K={K} b_col={b_col}")
+
+
 @pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
 def test_thousand_cubed_every_layout(in_t, out_t):
     M = N = K = 1000
