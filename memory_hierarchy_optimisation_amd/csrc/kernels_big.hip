@@ -56,11 +56,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
 }
 
 // Byte offset of 16-byte chunk c (0..7) of row r in a K-contiguous 256 x 64 tile (128
-// bytes a row).  The LDS serves a 16-byte-per-lane access 16 lanes at a time from 64
-// four-byte banks, i.e. 16 distinct 16-byte slots (address / 16 mod 16) per cycle.
-// Row r starts at slot 8 (r % 2); XOR-ing the chunk with (r / 2) % 8 makes the 16
-// rows r0 .. r0 + 15 (r0 even) read at one chunk column land on 16 distinct slots.
-__device__ __forceinline__ int koff(int r, int c) { return r * 128 + ((c ^ ((r >> 1) & 7)) << 4); }
+// bytes a row), chunks XOR-swizzled per row.  The LDS serves a 16-byte-per-lane access
+// 16 lanes at a time from 64 four-byte banks, i.e. 16 distinct 16-byte slots (address
+// / 16 mod 16) per cycle; row r starts at slot 8 (r % 2).  The swizzle depends on bits
+// 1..4 of r only, so it repeats every 32 rows (a row-block step is a plain offset of
+// 4096 bytes), and it spreads over 16 distinct slots both
+//   * 16 consecutive rows read at one chunk column (the fragment reads), and
+//   * the transposed stores of row-major B (16 lanes: 4 k-chunks x 4 n-rows 8 apart,
+//     see GeoBn), which is what its bit-4 term is for.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) & 7) ^ ((r >> 2) & 4); }
+__device__ __forceinline__ int koff(int r, int c) { return r * 128 + ((c ^ swz(r)) << 4); }
 
 // LDS accesses through 32-bit LDS addresses, so that every per-lane address is one
 // register plus a constant the instruction's 16-bit offset field absorbs.
@@ -79,23 +84,25 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 }
 
 // Row-major B (N-contiguous in memory): lane t owns the 8 x 8 block of k-rows
-// 8*(t % 8) .. +7 and n-columns 8*(t / 8) .. +7 of the slab.  Load i reads k-row
-// 8*(t%8) + i; eight neighbouring lanes read eight k-rows, and the eight lane groups of
-// a wave read 128 contiguous bytes of each.  The block is transposed in registers and
-// stored as 8 n-rows of 8 k-values: n-row 8*(t/8) + j, k-chunk t % 8.
+// 8 kg .. +7 and n-columns 8 nc .. +7 of the slab, with (lane l = t % 64 of wave
+// w = t / 64) m = l % 4, kg = (l / 4) % 8, nc = 8 w + 4 (l / 32) + m.  Load i reads
+// k-row 8 kg + i: every four consecutive lanes read 64 contiguous bytes of one row, so
+// a quad of lanes touches one cache line.  The block is transposed in registers and
+// stored as 8 n-rows of 8 k-values (n-row 8 nc + jj, k-chunk kg).
 struct GeoBn {
-  uint32_t off;        // byte offset of k-row 8*(t%8), n-chunk t/8
+  uint32_t off;        // byte offset of k-row 8 kg, n-chunk nc
   uint32_t stride;     // one k-row, in bytes
-  int klim;            // k-rows of the matrix at and below 8*(t%8); very negative if the
+  int klim;            // k-rows of the matrix at and below 8 kg; very negative if the
                        // lane's columns lie past N
   uint32_t st_base;    // see store_one
   uint32_t sel[2];     // byte selectors of store_one for even and odd j
   __device__ __forceinline__ void init(int64_t ldb, int n0, int64_t N, int64_t K) {
-    const int kg = threadIdx.x % 8, nc = threadIdx.x / 8, par = nc & 1;
+    const int w = threadIdx.x / 64, l = threadIdx.x % 64;
+    const int m = l % 4, kg = (l / 4) % 8, nc = 8 * w + 4 * (l / 32) + m, par = m & 1;
     off = uint32_t((int64_t(8 * kg) * ldb + 8 * nc) * 2);
     stride = uint32_t(ldb * 2);
     klim = n0 + 8 * nc < N ? int(min<int64_t>(K - 8 * kg, 1 << 30)) : -(1 << 30);
-    st_base = uint32_t(1024 * nc) | uint32_t(128 * par) | uint32_t((kg ^ (4 * par)) << 4);
+    st_base = uint32_t(1024 * nc) | uint32_t(128 * par) | uint32_t((kg ^ (4 * ((m ^ (m >> 1)) & 1))) << 4);
     // low halves of both words for an even n-row, high halves for an odd one
     sel[0] = par ? 0x07060302u : 0x05040100u;
     sel[1] = par ? 0x05040100u : 0x07060302u;
@@ -106,17 +113,18 @@ struct GeoBn {
   __device__ __forceinline__ u32x4 load_one(__amdgpu_buffer_rsrc_t rs, int k0, int i) const {
     return __builtin_amdgcn_raw_buffer_load_b128(rs, i < klim - k0 ? off : kOut, int(i * stride), 0);
   }
-  // Store j writes n-row jj = j ^ (n-chunk parity) of the lane's block, so that the 16
-  // lanes of an LDS cycle (two n-chunks) cover rows of both parities and 16 distinct
-  // slots.  Its offset koff(8 nc + jj, kg) = 1024 nc + 128 jj + 16 (kg ^ 4 (nc % 2)
-  // ^ j / 2) is st_base ^ (128 j + 16 (j / 2)); `base` is st_base.  jj and j share the
-  // register word j / 2; the half is picked per lane by the selector.
+  // Store j writes n-row jj = j ^ (m % 2) of the lane's block: the 16 lanes of an LDS
+  // cycle (k-chunks kg..kg+3, four n-chunks) so cover rows of both parities and, with
+  // the swizzle, 16 distinct slots.  Its offset koff(8 nc + jj, kg) is
+  // st_base ^ (128 j + 16 (j / 2)), st_base = 1024 nc | 128 (m % 2) |
+  // 16 (kg ^ 4 ((m ^ m / 2) % 2)); `base` is st_base.  jj and j share the register word
+  // j / 2; the half is picked per lane by the selector.
   __device__ __forceinline__ void store_one(const u32x4 (&r)[8], uint32_t base, uint32_t tile, int j) const {
     const uint32_t s = sel[j & 1];
     const int w = j >> 1;
     u32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)   // k = 8 (t%8) + 2e (low half) and 8 (t%8) + 2e + 1 (high half)
+    for (int e = 0; e < 4; ++e)   // k = 8 kg + 2e (low half) and 8 kg + 2e + 1 (high half)
       v[e] = __builtin_amdgcn_perm(r[2 * e + 1][w], r[2 * e][w], s);
     lds_st((base ^ uint32_t(128 * j + 16 * (j >> 1))) + tile, v);
   }
@@ -153,7 +161,7 @@ struct GeoBk {
 // A's slab (K-contiguous) loaded straight into LDS.  A load instruction of a wave
 // fills 64 consecutive 16-byte slots: load j of wave w covers rows 32 j + 8 w .. +7,
 // lane l the row 32 j + 8 w + l / 8 and LDS slot l % 8 of it, which holds the row's
-// k-chunk (l % 8) ^ ((row / 2) % 8) -- the XOR swizzle of koff applied on the global side.
+// k-chunk (l % 8) ^ swz(row) -- the XOR swizzle of koff applied on the global side.
 struct DmaA {
   uint32_t off;        // byte offset of this lane's chunk for j = 0, from the slab origin
   uint32_t stride;     // 32 rows, in bytes
@@ -161,7 +169,7 @@ struct DmaA {
   int klim;            // slabs with k0 < klim have this lane's chunk inside K
   __device__ __forceinline__ void init(int64_t lda, int m0, int64_t M, int64_t K) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int row = 8 * wave + lane / 8, c = (lane % 8) ^ ((row >> 1) & 7);
+    const int row = 8 * wave + lane / 8, c = (lane % 8) ^ swz(row);
     off = uint32_t((int64_t(row) * lda + 8 * c) * 2);
     stride = uint32_t(32 * lda * 2);
     rows_left = int(min<int64_t>(M - m0 - row, 1 << 30));
@@ -214,7 +222,7 @@ struct BigGemm {
   uint32_t fa_base, fb_base;     // koff of the lane's fragment rows for k-half 0
   DmaA da;
   GeoB gb;
-  u32x4 rb[2][8];                // B register sets: slab s is staged in set s % 2
+  u32x4 rb[4][8];                // B register sets: slab s is staged in set s % 4
   f32x16 acc[4][4];
   // Fragments of one k-half (16 deep): 4 row blocks of A, 4 column blocks of B.  Phase
   // p of a slab multiplies the half in set p % 2 while the next half is read into the
@@ -274,15 +282,26 @@ struct BigGemm {
   // saturates at 15, and without that wait a fragment consumed late in a phase would
   // also wait for the reads and writes issued early in it.
   //
-  // BS = (t + 1) % 2.  On entry: fragment set 0 holds k-half 0 of slab t; A slab t is
-  // in LDS and A slab t+1 in flight; B slab t is in LDS, B slab t+1 in register set BS
-  // and slab t+2 in set 1 - BS (loads possibly in flight).
-  template <int BS>
+  // Global traffic is spread evenly, four loads per wave and phase: A slab t+2 in
+  // phases 0 and 1 (into the ring slot of slab t-1, free since the previous barrier;
+  // it must have landed by the barrier of slab t+1), B slab t+4 in phases 2 and 3 into
+  // register set t % 4, which slab t left in the previous slab.  B slab t+1 is
+  // transposed out of its set into its LDS slot over phases 0..2.
+  //
+  // S = t % 4.  On entry: fragment set 0 holds k-half 0 of slab t; A slab t is in LDS
+  // and A slab t+1 in flight; B slab t is in LDS and slabs t+1..t+3 are in (or on their
+  // way into) register sets (S+1..S+3) % 4.
+  template <int S>
   __device__ __forceinline__ void slab(int t) {
+    constexpr int BS = (S + 1) & 3;                 // register set of B slab t+1
     const uint32_t ab = opaque(fa_base), bb = opaque(fb_base), sbase = opaque(gb.st_base);
-    const uint32_t ca = a_slot(t), cb = lds0 + (1 - BS) * TILE_BYTES, nb = lds0 + BS * TILE_BYTES;
-    // Phase 0: B slab t+1 out of register set BS into its LDS slot (slab t-1's, whose
-    // readers all passed the previous barrier).
+    const uint32_t ca = a_slot(t), cb = lds0 + (S & 1) * TILE_BYTES, nb = lds0 + ((S + 1) & 1) * TILE_BYTES;
+    const int ka = (t + 2) * BK, kb = (t + 4) * BK;
+    const __amdgpu_buffer_rsrc_t ra = da.rsrc(A, p.lda, m0, ka);
+    const __amdgpu_buffer_rsrc_t rbs = gb.rsrc(B, p.ldb, n0, kb);
+    const int la = da.lim(ka);
+    const uint32_t adst = a_slot(t + 2);
+    // Phase 0: A loads 0..3, B stores 0..2.
     wait_lgkm0();
     MHG_ORDER();
     {
@@ -292,47 +311,44 @@ struct BigGemm {
         mma<0>(2 * k); MHG_ORDER();
         read_one<1>(xa, xb, k); MHG_ORDER();
         mma<0>(2 * k + 1); MHG_ORDER();
-        gb.store_one(rb[BS], sbase, nb, k); MHG_ORDER();
+        if (k % 2 == 0) { da.issue_one(ra, la, adst, wave, k / 2); MHG_ORDER(); }
+        else if (k < 7) { gb.store_one(rb[BS], sbase, nb, k / 2); MHG_ORDER(); }
       }
     }
-    // Phase 1: A slab t+2 requested into the ring slot slab t-1 used.
+    // Phase 1: A loads 4..7, B stores 3..5.
     wait_lgkm0();
     MHG_ORDER();
     {
       const uint32_t xa = half_off(ab, 2, ca), xb = half_off(bb, 2, cb);
-      const int k0 = (t + 2) * BK;
-      const __amdgpu_buffer_rsrc_t rs = da.rsrc(A, p.lda, m0, k0);
-      const int l = da.lim(k0);
-      const uint32_t dst = a_slot(t + 2);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         mma<1>(2 * k); MHG_ORDER();
         read_one<0>(xa, xb, k); MHG_ORDER();
         mma<1>(2 * k + 1); MHG_ORDER();
-        da.issue_one(rs, l, dst, wave, k); MHG_ORDER();
+        if (k % 2 == 0) { da.issue_one(ra, la, adst, wave, 4 + k / 2); MHG_ORDER(); }
+        else if (k < 7) { gb.store_one(rb[BS], sbase, nb, 3 + k / 2); MHG_ORDER(); }
       }
     }
-    // Phase 2: register set BS refilled with B slab t+3.
+    // Phase 2: B loads 0..3 of slab t+4, B stores 6 and 7.
     wait_lgkm0();
     MHG_ORDER();
     {
       const uint32_t xa = half_off(ab, 3, ca), xb = half_off(bb, 3, cb);
-      const int k0 = (t + 3) * BK;
-      const __amdgpu_buffer_rsrc_t rs = gb.rsrc(B, p.ldb, n0, k0);
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         mma<0>(2 * k); MHG_ORDER();
         read_one<1>(xa, xb, k); MHG_ORDER();
         mma<0>(2 * k + 1); MHG_ORDER();
-        rb[BS][k] = gb.load_one(rs, k0, k); MHG_ORDER();
+        if (k % 2 == 0) { rb[S][k / 2] = gb.load_one(rbs, kb, k / 2); MHG_ORDER(); }
+        else if (k < 5) { gb.store_one(rb[BS], sbase, nb, 6 + k / 2); MHG_ORDER(); }
       }
     }
-    // A slab t+1 landed: the loads issued after its last one are slab t-1's 8 B loads
-    // and this slab's 8 A and 8 B loads.  Every wave stored B slab t+1 and finished
-    // reading slab t.
-    wait_vm_lgkm_barrier<24>();
+    // A slab t+1 landed: the loads issued after its last one are slab t-1's 8 B loads,
+    // this slab's 8 A loads and its first 4 B loads.  Every wave stored B slab t+1 and
+    // finished reading slab t.
+    wait_vm_lgkm_barrier<20>();
     MHG_ORDER();
-    // Phase 3: k-half 0 of slab t+1 read.
+    // Phase 3: k-half 0 of slab t+1 read; B loads 4..7 of slab t+4.
     {
       const uint32_t xa = half_off(ab, 0, a_slot(t + 1)), xb = half_off(bb, 0, nb);
 #pragma unroll
@@ -340,6 +356,7 @@ struct BigGemm {
         mma<1>(2 * k); MHG_ORDER();
         read_one<0>(xa, xb, k); MHG_ORDER();
         mma<1>(2 * k + 1); MHG_ORDER();
+        if (k % 2 == 0) { rb[S][4 + k / 2] = gb.load_one(rbs, kb, 4 + k / 2); MHG_ORDER(); }
       }
     }
   }
@@ -367,28 +384,38 @@ struct BigGemm {
       for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
     // Prologue: B slab 0 through set 0 into slot 0, A slabs 0 and 1 requested, B slabs
-    // 1 and 2 into sets 1 and 0.  Past K every load reads zeros, so the loop body has
-    // no branches and issues the same loads in every slab.
+    // 1..3 into sets 1..3, in the order the loop's waits assume (A slab 1 before the
+    // last eight B loads).  Past K every load reads zeros, so the loop body has no
+    // branches and issues the same loads in every slab.
     load_b<0>(0);
     da.issue(A, p.lda, m0, 0, a_slot(0), wave);
+    load_b<1>(BK);
+    load_b<2>(2 * BK);
     wait_vm0();
     store_b<0>(gb.st_base, lds0);
-    load_b<1>(BK);
     da.issue(A, p.lda, m0, BK, a_slot(1), wave);
-    load_b<0>(2 * BK);
-    wait_vm_lgkm_barrier<24>();    // A slab 0 came before the wait above
+    load_b<3>(3 * BK);
+    wait_vm_lgkm_barrier<16>();    // A slab 0 came before the wait above
     read_half<0>(fa_base, fb_base, a_slot(0), lds0, 0);
 
-    // Two slabs per trip (register-set and LDS-slot indices are compile-time), the odd
-    // one out peeled: a conditional second slab inside the loop would merge two copies
-    // of the 256 accumulators at its end, which the register allocator resolves with
-    // spills.
+    // Four slabs per trip (register-set and LDS-slot indices are compile-time); the
+    // last KT % 4 slabs are peeled.  A conditional slab inside the loop would merge two
+    // copies of the 256 accumulators at the loop's end, which the register allocator
+    // resolves with spills.
     int t = 0;
-    for (; t + 1 < KT; t += 2) {
-      slab<1>(t);
-      slab<0>(t + 1);
+    for (; t + 3 < KT; t += 4) {
+      slab<0>(t);
+      slab<1>(t + 1);
+      slab<2>(t + 2);
+      slab<3>(t + 3);
     }
-    if (t < KT) slab<1>(t);
+    if (t < KT) {
+      slab<0>(t);
+      if (t + 1 < KT) {
+        slab<1>(t + 1);
+        if (t + 2 < KT) slab<2>(t + 2);
+      }
+    }
     // Loads still in flight write LDS: drain them before the workgroup ends.
     wait_vm0();
 
