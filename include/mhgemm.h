@@ -97,6 +97,16 @@ enum gemm_kind {
  * Returns NULL on invalid arguments (message via gemm_last_error).  A plan for
  * M == 0 or N == 0 runs as a no-op; a plan for K == 0 fills C with zeros (the
  * empty sum).
+ *
+ * M <= 16 (fp16 / bf16, row-major A and B, K, N, lda, ldb multiples of 8) selects
+ * GEMM_KIND_SKINNY: such a product streams B once and is bound by HBM bandwidth
+ * ("Tiling 策略与内存层次优化", roofline: intensity far left of the ridge), so K is
+ * also split across workgroups until every compute unit holds one ("GPU Kernel 的
+ * Tile、Grid、Wave 与 Launch Overhead", per-shape section: too few workers).  With a
+ * split factor above 1 the plan owns a device workspace of arrival counters and fp32
+ * partials (gemm_plan_describe field 15), allocated on the current device here when
+ * one is present (otherwise on the first gemm_run) and freed by gemm_destroy; it
+ * returns NULL (GEMM_ERR_ALLOC message) when that allocation fails.
  */
 gemm_plan_t gemm_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                       int dtype, int layout);
@@ -121,8 +131,12 @@ gemm_plan_t gemm_plan_config(int64_t M, int64_t N, int64_t K, int64_t lda, int64
  * top of this file.  Pointers need only element alignment: operands whose base
  * address, leading dimension or contiguous extent is not a multiple of 16 bytes
  * are staged with narrower loads.  NULL operands are rejected when the operand has
- * elements to read or write.  Returns GEMM_OK, GEMM_ERR_INVALID_ARG, or
- * GEMM_ERR_HIP when the launch itself fails.  Never synchronises.
+ * elements to read or write.  Returns GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_HIP
+ * when the launch itself fails, GEMM_ERR_ALLOC when a split-K workspace deferred from
+ * gemm_plan cannot be allocated (that first run allocates; later runs do not), or
+ * GEMM_ERR_UNSUPPORTED when the plan's workspace lives on another device than the
+ * current one.  Never synchronises otherwise.  Split-K results are reproducible bit
+ * for bit: partials are added in a fixed order whatever the workgroups' order.
  */
 int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stream);
 

@@ -21,10 +21,14 @@ hipError_t launch_fill(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_ring(int launcher, const LaunchArgs &p, hipStream_t s);
 bool ring_supported(const LaunchArgs &p, int bm, int bn);
 hipError_t launch_big(const LaunchArgs &p, hipStream_t s);
+hipError_t launch_skinny(const LaunchArgs &p, hipStream_t s);
+hipError_t launch_zero_words(void *w, int64_t n, hipStream_t s);
 }  // namespace mhg
 
 struct gemm_plan_s {
   mhg::PlanData d;
+  void *ws = nullptr;   // split-K workspace (device memory), or NULL
+  int ws_dev = -1;      // device it lives on
 };
 
 namespace {
@@ -47,6 +51,10 @@ mhg::Hardware query_hardware() {
   return hw;
 }
 
+// 32-bit arrival counters at the start of a split-K workspace (one per column block,
+// padded to 256 bytes).
+int64_t counter_words(const mhg::PlanData &d) { return (int64_t(d.gn) * 4 + 255) / 256 * 64; }
+
 gemm_plan_t make_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
                       int dtype, int layout, const int32_t *cfg) {
   mhg::PlanData d;
@@ -67,8 +75,53 @@ gemm_plan_t make_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
     return nullptr;
   }
   plan->d = d;
+  // A workspace is allocated here when a device is present (its arrival counters
+  // zeroed), else on the plan's first run.
+  int dev = -1;
+  if (d.ws_bytes > 0 && hipGetDevice(&dev) == hipSuccess) {
+    if (hipMalloc(&plan->ws, size_t(d.ws_bytes)) != hipSuccess ||
+        hipMemset(plan->ws, 0, size_t(counter_words(d)) * 4) != hipSuccess) {
+      (void)hipGetLastError();
+      if (plan->ws) (void)hipFree(plan->ws);
+      delete plan;
+      set_error("gemm_plan: cannot allocate the split-K workspace");
+      return nullptr;
+    }
+    plan->ws_dev = dev;
+  }
+  (void)hipGetLastError();
   set_error("");
   return plan;
+}
+
+// Make sure the plan's workspace exists on the current device (first run of a plan
+// made without a device).  Returns a gemm_status.
+int ensure_workspace(gemm_plan_s *plan, hipStream_t s) {
+  if (plan->d.ws_bytes == 0) return GEMM_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    set_error("gemm_run: no current HIP device");
+    return GEMM_ERR_HIP;
+  }
+  if (plan->ws) {
+    if (dev != plan->ws_dev) {
+      set_error("gemm_run: the plan's split-K workspace lives on another device");
+      return GEMM_ERR_UNSUPPORTED;
+    }
+    return GEMM_OK;
+  }
+  if (hipMalloc(&plan->ws, size_t(plan->d.ws_bytes)) != hipSuccess) {
+    (void)hipGetLastError();
+    plan->ws = nullptr;
+    set_error("gemm_run: cannot allocate the split-K workspace");
+    return GEMM_ERR_ALLOC;
+  }
+  plan->ws_dev = dev;
+  if (mhg::launch_zero_words(plan->ws, counter_words(plan->d), s) != hipSuccess) {
+    set_error("gemm_run: cannot clear the split-K workspace");
+    return GEMM_ERR_HIP;
+  }
+  return GEMM_OK;
 }
 
 }  // namespace
@@ -132,11 +185,20 @@ int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stre
     int count;
     const mhg::Variant *cat = mhg::catalogue(&count);
     const mhg::Variant *v = &cat[d.variant];
-    if (v->fallback >= 0 && !mhg::ring_supported(a, v->cfg.bm, v->cfg.bn)) {
-      v = mhg::variant_of_launcher(v->fallback);   // same tile, register-staged: any alignment
+    const bool direct_ok = v->launcher == mhg::L_SKINNY ? (a.vec_a && a.vec_b)
+                                                        : mhg::ring_supported(a, v->cfg.bm, v->cfg.bn);
+    if (v->fallback >= 0 && !direct_ok) {
+      v = mhg::variant_of_launcher(v->fallback);   // register-staged: any alignment
       a.gm = int((d.M + v->cfg.bm - 1) / v->cfg.bm);
       a.gn = int((d.N + v->cfg.bn - 1) / v->cfg.bn);
       a.group_m = std::max(1, std::min(a.gm, 4));
+      a.split_k = 1;
+    }
+    if (v->launcher == mhg::L_SKINNY && a.split_k > 1) {
+      const int st = ensure_workspace(plan, s);
+      if (st != GEMM_OK) return st;
+      a.workspace = plan->ws;
+      a.ws_bytes = d.ws_bytes;
     }
     switch (v->launcher) {
       case mhg::L_FMA_32: case mhg::L_FMA_64: case mhg::L_FMA_128:
@@ -145,6 +207,8 @@ int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stre
         e = mhg::launch_ring(v->launcher, a, s); break;
       case mhg::L_BIG_256:
         e = mhg::launch_big(a, s); break;
+      case mhg::L_SKINNY:
+        e = mhg::launch_skinny(a, s); break;
       default:
         e = mhg::launch_mfma(v->launcher, a, s); break;
     }
@@ -156,7 +220,12 @@ int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stre
   return GEMM_OK;
 }
 
-void gemm_destroy(gemm_plan_t plan) { delete plan; }
+void gemm_destroy(gemm_plan_t plan) {
+  if (!plan) return;
+  if (plan->ws) (void)hipFree(plan->ws);
+  (void)hipGetLastError();
+  delete plan;
+}
 
 const char *gemm_last_error(void) { return g_last_error.c_str(); }
 

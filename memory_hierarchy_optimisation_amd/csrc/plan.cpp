@@ -45,6 +45,12 @@ const Variant kCatalogue[] = {
     {{GEMM_KIND_MFMA, 256, 256, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_256x256_W4, 8, 8, L_MFMA_256x256},
     {{GEMM_KIND_MFMA, 256, 256, 32, 2, 4, 4, 1}, 512, kHalf, L_RING_256x256_W8, 8, 4, L_MFMA_256x256},
     {{GEMM_KIND_MFMA, 256, 256, 64, 2, 4, 2, 1}, 512, kHalf, L_MFMA_256x256, 8, 4, -1},
+    // M <= 16: one workgroup per 128 columns and K chunk (split-K factor last).
+    {{GEMM_KIND_SKINNY, 16, 128, 32, 1, 4, 2, 1}, 256, kHalf, L_SKINNY, 1, 8, L_MFMA_64x64},
+    {{GEMM_KIND_SKINNY, 16, 128, 32, 1, 4, 2, 2}, 256, kHalf, L_SKINNY, 1, 8, L_MFMA_64x64},
+    {{GEMM_KIND_SKINNY, 16, 128, 32, 1, 4, 2, 4}, 256, kHalf, L_SKINNY, 1, 8, L_MFMA_64x64},
+    {{GEMM_KIND_SKINNY, 16, 128, 32, 1, 4, 2, 8}, 256, kHalf, L_SKINNY, 1, 8, L_MFMA_64x64},
+    {{GEMM_KIND_SKINNY, 16, 128, 32, 1, 4, 2, 16}, 256, kHalf, L_SKINNY, 1, 8, L_MFMA_64x64},
 };
 
 bool is_ring(int launcher) {
@@ -65,6 +71,7 @@ double best_intensity(int elem, unsigned mask) {
 // MFMA: 4 fp32 per 16x16 block + fragments + staged 16-byte chunks.
 int regs_estimate(const Variant &v) {
   if (v.launcher == L_BIG_256) return 512;   // one wave per SIMD: 256 accumulators in AGPRs
+  if (v.launcher == L_SKINNY) return 128;    // 8 accumulators, two staged rounds, transposes
   if (is_ring(v.launcher)) {   // accumulators + two fragment sets + addressing
     return v.tm * v.tn * 4 + 2 * (v.tm + v.tn) * 4 + 24;
   }
@@ -117,6 +124,7 @@ double tile_intensity(int bm, int bn, int elem) {
 // pad each k-row by four elements.
 static int64_t lds_allocated(const Variant &v, int elem) {
   const TileConfig &c = v.cfg;
+  if (v.launcher == L_SKINNY) return int64_t(4) * 16 * c.bn * 4 + 16;   // wave partials, flag
   if (c.kind == GEMM_KIND_FMA)
     return (int64_t(c.bm + 4) * c.bk + int64_t(c.bn + 4) * c.bk) * elem * c.stages;
   return lds_bytes_of(c, elem);
@@ -199,8 +207,31 @@ bool ring_shape_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bo
 
 bool needs_aligned_staging(int launcher) { return is_ring(launcher) || launcher == L_BIG_256; }
 
+bool skinny_shape_ok(const PlanData &p, std::string *why) {
+  const char *msg = nullptr;
+  if (p.M > 16) msg = "variant for at most 16 rows of A";
+  else if (p.layout & (GEMM_A_COL | GEMM_B_COL)) msg = "variant for at most 16 rows needs row-major A and B";
+  else if (p.K % 8 || p.N % 8 || p.lda % 8 || p.ldb % 8)
+    msg = "variant with direct 16-byte staging needs extents and leading dimensions that are multiples of 8";
+  else if (p.K >= (int64_t(1) << 30) || p.lda >= (int64_t(1) << 25) || p.ldb >= (int64_t(1) << 25))
+    msg = "variant for at most 16 rows needs K < 2^30 and leading dimensions below 2^25";
+  if (msg && why) *why = msg;
+  return msg == nullptr;
+}
+
+int skinny_split(const PlanData &p, const Hardware &hw) {
+  // More workgroups until every compute unit holds one (each keeps two rounds per
+  // wave in flight, enough to cover the HBM latency; more chunks only add partials
+  // to reduce), while each K chunk keeps at least 512 k (four rounds a wave).
+  const int64_t gn = (p.N + 127) / 128;
+  int s = 1;
+  while (s < 16 && gn * s < int64_t(hw.cus) && p.K / (2 * s) >= 512) s *= 2;
+  return s;
+}
+
 double score(const Variant &v, const PlanData &p, const Hardware &hw, std::string *why) {
   const int elem = elem_bytes(p.in_code);
+  if (v.launcher == L_SKINNY && !skinny_shape_ok(p, why)) return -1.0;
   if (v.launcher == L_BIG_256 && (p.layout & GEMM_A_COL)) {
     if (why) *why = "256x256 four-wave variant needs row-major A";
     return -1.0;
@@ -255,6 +286,8 @@ static void fill_plan(PlanData *p, int idx, const Hardware &hw) {
   // row-panels and B column-panels in L2.
   p->group_m = std::max(1, std::min(p->gm, 4));
   p->ws_bytes = 0;
+  if (v.launcher == L_SKINNY && v.cfg.split_k > 1)   // arrival counters, then partials
+    p->ws_bytes = (int64_t(p->gn) * 4 + 255) / 256 * 256 + int64_t(v.cfg.split_k) * p->gn * 16 * v.cfg.bn * 4;
 }
 
 bool select(PlanData *p, const Hardware &hw, std::string *err) {
@@ -270,9 +303,20 @@ bool select(PlanData *p, const Hardware &hw, std::string *err) {
   }
   int n;
   const Variant *cat = catalogue(&n);
+  // At most 16 rows: the product streams B once and is bound by HBM, not by tile
+  // reuse, so the split-K kernel is taken whenever it applies.
+  if (p->M <= 16 && (1u << p->in_code) & kHalf && skinny_shape_ok(*p, nullptr)) {
+    const int split = skinny_split(*p, hw);
+    for (int i = 0; i < n; ++i)
+      if (cat[i].launcher == L_SKINNY && cat[i].cfg.split_k == split && score(cat[i], *p, hw, nullptr) >= 0.0) {
+        fill_plan(p, i, hw);
+        return true;
+      }
+  }
   int best = -1;
   double best_score = -1.0;
   for (int i = 0; i < n; ++i) {
+    if (cat[i].launcher == L_SKINNY) continue;
     double s = score(cat[i], *p, hw, nullptr);
     if (s > best_score + 1e-12) {
       best_score = s;

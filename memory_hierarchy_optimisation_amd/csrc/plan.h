@@ -55,6 +55,13 @@ bool ring_shape_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bo
 // Variants with a fallback need direct 16-byte staging; the plan checks what it can see
 // (extents and leading dimensions), gemm_run checks pointer alignment.
 bool needs_aligned_staging(int launcher);
+// The split-K variant for at most 16 rows: the shape rules, and the split factor the
+// selector takes (powers of two up to 16, one workgroup per compute unit, K chunks of
+// at least 512).
+struct PlanData;
+bool skinny_shape_ok(const PlanData &p, std::string *why);
+struct Hardware;
+int skinny_split(const PlanData &p, const Hardware &hw);
 
 // Hardware description used by the resource model.
 struct Hardware {

@@ -108,6 +108,10 @@ def test_grid_and_lds_follow_the_formulas(M, N, K, dtype, layout):
     formula = F.smem_bytes(d["bm"], d["bn"], d["bk"], elem, d["stages"])
     if d["kind"] == mh.GEMM_KIND_MFMA:
         assert d["lds_bytes"] == formula          # swizzled, no padding
+    elif d["kind"] == mh.GEMM_KIND_SKINNY:
+        # no staged slabs: LDS holds the four waves' 16 x BN fp32 partials and a flag
+        assert d["lds_bytes"] == 4 * 16 * d["bn"] * 4 + 16
+        assert d["grid_z"] == d["split_k"]
     else:
         assert formula <= d["lds_bytes"] <= formula * 1.2   # k-rows padded by 4 floats
     assert d["lds_bytes"] <= 160 * 1024
@@ -135,6 +139,55 @@ def test_forced_configuration_checks():
         _plan(300, 300, 300, mh.GEMM_F32_F32, cfg=(2, 128, 128, 64, 2, 2, 2, 1))
     with pytest.raises(mh.GemmError, match="input type"):
         _plan(300, 300, 300, mh.GEMM_BF16_F32, cfg=(1, 64, 64, 16, 4, 1, 2, 1))
+
+
+SKINNY_WS = lambda gn, split: (0 if split == 1 else (gn * 4 + 255) // 256 * 256 + split * gn * 16 * 128 * 4)
+
+
+@pytest.mark.parametrize("M,N,K,split", [
+    (16, 8192, 8192, 4),     # 64 column blocks x 4 chunks = one workgroup per compute unit
+    (4, 256, 8192, 16),      # two column blocks: the largest split
+    (16, 8192, 1024, 2),     # K chunks stop at 512
+    (1, 32768, 4096, 1),     # 256 column blocks already fill the chip
+])
+def test_skinny_products_split_k_across_workgroups(M, N, K, split):
+    d = _plan(M, N, K, mh.GEMM_BF16_F32)
+    gn = (N + 127) // 128
+    assert d["kind"] == mh.GEMM_KIND_SKINNY
+    assert (d["bm"], d["bn"], d["split_k"]) == (16, 128, split)
+    assert (d["grid_x"], d["grid_y"], d["grid_z"]) == (1, gn, split)
+    assert d["workspace_bytes"] == SKINNY_WS(gn, split)
+
+
+@pytest.mark.parametrize("M,N,K,dtype,layout,lda,ldb", [
+    (17, 8192, 8192, mh.GEMM_BF16_F32, 0, None, None),   # more than 16 rows
+    (16, 8192, 8196, mh.GEMM_BF16_F32, 0, 8200, None),   # K not a multiple of 8
+    (16, 8190, 8192, mh.GEMM_BF16_F32, 0, None, None),   # N not a multiple of 8
+    (16, 8192, 8192, mh.GEMM_BF16_F32, 1, 16, None),     # column-major A
+    (16, 8192, 8192, mh.GEMM_BF16_F32, 2, None, 8192),   # column-major B
+    (16, 8192, 8192, mh.GEMM_F32_F32, 0, None, None),    # fp32 inputs
+])
+def test_skinny_variant_only_where_it_applies(M, N, K, dtype, layout, lda, ldb):
+    kw = {}
+    if lda is not None:
+        kw["lda"] = lda
+    if ldb is not None:
+        kw["ldb"] = ldb
+    d = _plan(M, N, K, dtype, layout, **kw)
+    assert d["kind"] != mh.GEMM_KIND_SKINNY
+
+
+def test_forced_skinny_configurations():
+    for split in (1, 2, 4, 8, 16):
+        d = _plan(8, 1024, 4096, mh.GEMM_F16_F16, cfg=(3, 16, 128, 32, 1, 4, 2, split))
+        assert (d["kind"], d["split_k"], d["grid_z"]) == (mh.GEMM_KIND_SKINNY, split, split)
+        assert d["workspace_bytes"] == SKINNY_WS(8, split)
+    with pytest.raises(mh.GemmError, match="at most 16 rows"):
+        _plan(17, 1024, 4096, mh.GEMM_F16_F16, cfg=(3, 16, 128, 32, 1, 4, 2, 2))
+    with pytest.raises(mh.GemmError, match="multiples of 8"):
+        _plan(8, 1024, 4092, mh.GEMM_F16_F16, cfg=(3, 16, 128, 32, 1, 4, 2, 2))
+    with pytest.raises(mh.GemmError, match="no compiled variant"):
+        _plan(8, 1024, 4096, mh.GEMM_F16_F16, cfg=(3, 16, 128, 32, 1, 4, 2, 3))
 
 
 def test_last_error_clears_on_success():

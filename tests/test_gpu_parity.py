@@ -172,6 +172,72 @@ def test_four_wave_256_kernel_every_slab_count(in_t, out_t, b_col):
         check_tolerance(C, Cref, out_t, f"K={K} b_col={b_col}")
 
 
+def SKINNY(split):
+    return (3, 16, 128, 32, 1, 4, 2, split)
+
+
+@pytest.mark.parametrize("in_t,out_t", HALF_DTYPES)
+def test_skinny_every_split_ragged(in_t, out_t):
+    """At most 16 rows: K split across 1..16 workgroup chunks (the last ones partly or
+    wholly past K), rows below 16, a last column block narrower than 128."""
+    for M, N, K in [(1, 136, 200), (5, 1000, 1032), (16, 264, 4104), (16, 4096, 64)]:
+        As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, seed=M + K)
+        Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t)
+        for split in (1, 2, 4, 8, 16):
+            C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, cfg=SKINNY(split))
+            assert (desc["kind"], desc["split_k"]) == (mh.GEMM_KIND_SKINNY, split)
+            check_tolerance(C, Cref, out_t, f"M={M} N={N} K={K} split={split}")
+
+
+@pytest.mark.parametrize("out_t", ["bf16", "f32"])
+def test_skinny_exact_integer_sums(out_t):
+    """Integer inputs: every partial sum (per wave, per workgroup, across chunks) is exact,
+    so the output is the oracle's rounding of the exact sum, bit for bit."""
+    M, N, K = 16, 1024, 8192
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "bf16", dist="int", r=2, seed=4)
+    Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16")
+    for split in (1, 8):
+        C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, "bf16", out_t, cfg=SKINNY(split))
+        check_exact(raw, Cref, out_t)
+
+
+def test_skinny_split_k_repeats_bit_for_bit():
+    """The last workgroup of a column block adds the chunks' partials in chunk order,
+    so repeated runs of one plan (which also re-arm the arrival counters) give the
+    same bits; a second plan with its own workspace agrees."""
+    w = synth.WORKLOADS["bf16_skinny"]
+    As, lda, Bs, ldb, _, _ = synth.workload_operands(w)
+    A, B = As.cuda(), Bs.cuda()
+    code = mh.DTYPE_OF[(w.dtype, w.out)]
+    outs = []
+    for _ in range(2):
+        plan = mh.gemm_plan(w.M, w.N, w.K, lda, ldb, w.N, code, 0)
+        try:
+            d = mh.gemm_plan_describe(plan)
+            assert d["kind"] == mh.GEMM_KIND_SKINNY and d["split_k"] > 1 and d["workspace_bytes"] > 0
+            for _ in range(3):
+                C = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+                mh.gemm_run(plan, A, B, C)
+                torch.cuda.synchronize()
+                outs.append(C.cpu())
+        finally:
+            mh.gemm_destroy(plan)
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int32), outs[0].view(torch.int32))
+    rows = (0, 3)
+    Cref = oracle_ref(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, rows=rows)
+    check_tolerance(outs[0][rows[0]:rows[1]].double().numpy(), Cref, "f32", "skinny rows")
+
+
+def test_skinny_falls_back_on_misaligned_pointers():
+    M, N, K = 16, 1024, 2048
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "f16", seed=12)
+    Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, "f16")
+    for oa, ob in [(1, 0), (0, 3)]:
+        C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "f16", "f32", cfg=SKINNY(4), offset_a=oa, offset_b=ob)
+        check_tolerance(C, Cref, "f32", f"offsets {oa} {ob}")
+
+
 @pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("f32", "f32")])
 def test_thousand_cubed_every_layout(in_t, out_t):
     M = N = K = 1000
