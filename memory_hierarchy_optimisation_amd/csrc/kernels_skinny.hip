@@ -45,6 +45,11 @@ constexpr int NT = 256;        // four waves
 constexpr int ROUND = 32;      // k per round and wave
 constexpr int CHUNK_ALIGN = 4 * ROUND;
 constexpr uint32_t kOut = 0x80000000u;   // beyond every buffer range: loads zeros
+constexpr int MAX_SPLIT = 16;
+// Cache-policy operand of the buffer instructions: B is streamed once (non-temporal);
+// the workspace partials use the device-scope coherence bit (sc1), the policy the
+// compiler gives agent-scope atomic loads and stores.
+constexpr int kNonTemporal = 2, kDeviceScope = 16;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
@@ -82,7 +87,7 @@ struct Skinny {
     const int lim = b_klim - kround;
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      rb[SET][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, i < lim ? b_off : kOut, int(i * b_row), 0);
+      rb[SET][i] = __builtin_amdgcn_raw_buffer_load_b128(rs, i < lim ? b_off : kOut, int(i * b_row), kNonTemporal);
     const __amdgpu_buffer_rsrc_t ar = rsrc_of(A + kr);
     ra[SET] = __builtin_amdgcn_raw_buffer_load_b128(ar, kround < a_klim ? a_off : kOut, 0, 0);
   }
@@ -182,17 +187,24 @@ struct Skinny {
     //
     // Visibility across the XCDs' separate L2 caches without a device-wide fence (an
     // agent-scope release writes back the whole L2 and cost more than the product
-    // itself once every workgroup issued one): the partials are written with
-    // agent-scope atomic stores, which write through to the coherent level; each lane
-    // waits for its stores to be acknowledged (vmcnt 0: the ordering part of a
-    // release, the L2 write-back part being needed only for ordinary stores); the
-    // workgroup barrier then precedes the arrival RMW, and the last arrival reads the
-    // partials back with agent-scope atomic loads, which are served from the coherent
-    // level, issued only after its RMW returned.
+    // itself once every workgroup issued one): the partials are written with the
+    // device-scope cache policy (sc1, as the compiler does for agent-scope atomic
+    // stores), which writes through to the coherent level; each lane waits for its
+    // stores to be acknowledged (vmcnt 0: the ordering part of a release, the L2
+    // write-back part being needed only for ordinary stores); the workgroup barrier
+    // then precedes the arrival RMW, and the last arrival reads the partials back with
+    // the same policy (served from the coherent level), issued only after its RMW
+    // returned.
     unsigned *count = static_cast<unsigned *>(p.workspace);
-    float *part = reinterpret_cast<float *>(static_cast<char *>(p.workspace) + ((int64_t(gn) * 4 + 255) / 256) * 256);
-    uint64_t *mine = reinterpret_cast<uint64_t *>(part + (int64_t(z) * gn + tn) * (16 * BN) + row * BN + col);
-    store_coherent(mine, s0, s1);
+    const float *part = reinterpret_cast<const float *>(static_cast<char *>(p.workspace) +
+                                                        ((int64_t(gn) * 4 + 255) / 256) * 256);
+    // One resource over the column block's partials: chunk zz at scalar offset
+    // zz * slice bytes (the plan keeps all partials below 2^31 bytes).
+    const __amdgpu_buffer_rsrc_t pr = rsrc_of(part + int64_t(tn) * (16 * BN));
+    const uint32_t slice = uint32_t(int64_t(gn) * (16 * BN) * 4);
+    const uint32_t voff = uint32_t((row * BN + col) * 4);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s0), pr, voff, int(z * slice), kDeviceScope);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, s1), pr, voff + 16, int(z * slice), kDeviceScope);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -201,40 +213,25 @@ struct Skinny {
     }
     __syncthreads();
     if (!*last) return;
-    const uint64_t *src = reinterpret_cast<const uint64_t *>(part + int64_t(tn) * (16 * BN) + row * BN + col);
-    const int64_t zstride = int64_t(gn) * (16 * BN) / 2;   // in 8-byte words
-    f32x4 t0, t1;
-    load_coherent(src, t0, t1);
-    for (int zz = 1; zz < split; ++zz) {
-      f32x4 u0, u1;
-      load_coherent(src + zz * zstride, u0, u1);
-      t0 += u0;
-      t1 += u1;
+    // All chunks' partials requested at once (chunks past split read zeros), then
+    // added in chunk order.
+    u32x4 v[MAX_SPLIT][2];
+#pragma unroll
+    for (int zz = 0; zz < MAX_SPLIT; ++zz) {
+      const uint32_t o = zz < split ? voff : kOut;
+      v[zz][0] = __builtin_amdgcn_raw_buffer_load_b128(pr, o, int(zz * slice), kDeviceScope);
+      v[zz][1] = __builtin_amdgcn_raw_buffer_load_b128(pr, o == kOut ? kOut : o + 16, int(zz * slice), kDeviceScope);
+    }
+    f32x4 t0 = __builtin_bit_cast(f32x4, v[0][0]), t1 = __builtin_bit_cast(f32x4, v[0][1]);
+#pragma unroll
+    for (int zz = 1; zz < MAX_SPLIT; ++zz) {
+      t0 += __builtin_bit_cast(f32x4, v[zz][0]);
+      t1 += __builtin_bit_cast(f32x4, v[zz][1]);
     }
     store(t0, t1);
     // Re-arm the counter for the next call on this workspace.
     if (threadIdx.x == 0) __hip_atomic_store(count + tn, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-
-  // Eight fp32 values through agent-scope atomic 8-byte stores / loads.
-  __device__ __forceinline__ static void store_coherent(uint64_t *w, f32x4 a, f32x4 b) {
-    __hip_atomic_store(w + 0, pack(a[0], a[1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(w + 1, pack(a[2], a[3]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(w + 2, pack(b[0], b[1]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(w + 3, pack(b[2], b[3]), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __device__ __forceinline__ static void load_coherent(const uint64_t *w, f32x4 &a, f32x4 &b) {
-    uint64_t v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = __hip_atomic_load(w + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    a = f32x4{lo(v[0]), hi(v[0]), lo(v[1]), hi(v[1])};
-    b = f32x4{lo(v[2]), hi(v[2]), lo(v[3]), hi(v[3])};
-  }
-  __device__ __forceinline__ static uint64_t pack(float x, float y) {
-    return uint64_t(__builtin_bit_cast(uint32_t, x)) | (uint64_t(__builtin_bit_cast(uint32_t, y)) << 32);
-  }
-  __device__ __forceinline__ static float lo(uint64_t v) { return __builtin_bit_cast(float, uint32_t(v)); }
-  __device__ __forceinline__ static float hi(uint64_t v) { return __builtin_bit_cast(float, uint32_t(v >> 32)); }
 };
 
 template <class H>

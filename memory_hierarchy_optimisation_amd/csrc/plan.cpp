@@ -213,8 +213,9 @@ bool skinny_shape_ok(const PlanData &p, std::string *why) {
   else if (p.layout & (GEMM_A_COL | GEMM_B_COL)) msg = "variant for at most 16 rows needs row-major A and B";
   else if (p.K % 8 || p.N % 8 || p.lda % 8 || p.ldb % 8)
     msg = "variant with direct 16-byte staging needs extents and leading dimensions that are multiples of 8";
-  else if (p.K >= (int64_t(1) << 30) || p.lda >= (int64_t(1) << 25) || p.ldb >= (int64_t(1) << 25))
-    msg = "variant for at most 16 rows needs K < 2^30 and leading dimensions below 2^25";
+  else if (p.K >= (int64_t(1) << 30) || p.lda >= (int64_t(1) << 25) || p.ldb >= (int64_t(1) << 25) ||
+           (p.N + 127) / 128 * 16 * 128 * 4 * 16 >= (int64_t(1) << 31))
+    msg = "variant for at most 16 rows needs K < 2^30, leading dimensions below 2^25 and N below 2^21";
   if (msg && why) *why = msg;
   return msg == nullptr;
 }
