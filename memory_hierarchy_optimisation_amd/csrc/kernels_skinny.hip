@@ -9,8 +9,9 @@
 // per-shape section: too few workers to hide latency) is more workers.  Along N alone
 // there are N / 128 column blocks (64 at N = 8192), a quarter of the compute units,
 // so K is split as well:
-//   * a workgroup owns 128 columns of C and one K chunk; its four waves take the
-//     chunk's 32-deep rounds in turn (wave w: rounds w, w+4, ...);
+//   * a workgroup owns 128 columns of C and every split-th 128-deep block of K (all
+//     workgroups then stream through the same window of B's rows); its four waves
+//     take one 32-deep round of each block;
 //   * the waves' partial sums are added in LDS in a fixed order;
 //   * with split_k > 1 each workgroup writes its 16 x 128 partial to the plan's
 //     workspace, and the last workgroup of a column block to arrive (a per-block
@@ -30,8 +31,8 @@
 // 16-byte load.  Two register sets keep the next round's loads in flight while one
 // is multiplied.
 //
-// Edges: rows of A at or beyond M, k-rows at or beyond the chunk end and column
-// chunks at or beyond N are loaded as zeros (buffer offsets beyond the resource
+// Edges: rows of A at or beyond M, k-rows at or beyond K and column chunks at or
+// beyond N are loaded as zeros (buffer offsets beyond the resource
 // range); stores are masked.  The kernel requires 16-byte aligned A and B with K, N,
 // lda and ldb multiples of 8 (checked by the host, which otherwise runs a
 // register-staged kernel instead).
@@ -55,24 +56,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
-// K chunk of a split: a multiple of four rounds, so that every wave of a workgroup
-// runs the same number of rounds.
-__host__ __device__ inline int64_t chunk_of(int64_t K, int split) {
-  const int64_t c = (K + split - 1) / split;
-  return (c + CHUNK_ALIGN - 1) / CHUNK_ALIGN * CHUNK_ALIGN;
-}
 
 template <class H>
 struct Skinny {
   const LaunchArgs &p;
   int lane, g, q;
-  // B: lane's byte offset (k-row 8 g, column chunk q) from a round's origin; k-rows
-  // left in the chunk below the lane's first row of round 0 (very negative when the
-  // lane's columns lie past N).
+  // B: lane's byte offset (k-row 8 g, column chunk q) from a round's origin; k-rows of
+  // the matrix at and below the lane's first row of round k = 0 (very negative when
+  // the lane's columns lie past N).
   uint32_t b_off, b_row;
   int b_klim;
-  // A: lane's byte offset (row q, k 8 g) from a round's origin; k left in the chunk
-  // at the lane's first k of round 0 (very negative when row q lies past M).
+  // A: lane's byte offset (row q, k 8 g) from a round's origin; k of the matrix at and
+  // beyond the lane's first k of round k = 0 (very negative when row q lies past M).
   uint32_t a_off;
   int a_klim;
   f32x4 acc[8];
@@ -117,37 +112,34 @@ struct Skinny {
     g = lane >> 4;
     q = lane & 15;
     const int64_t n0 = int64_t(tn) * BN;
-    const int64_t chunk = chunk_of(p.K, split);
-    const int64_t k_begin = int64_t(z) * chunk;
-    const int64_t k_end = min(p.K, k_begin + chunk);
-    const int rounds = int(chunk / CHUNK_ALIGN);     // rounds per wave
+    // The workgroup of chunk z takes the 128-deep blocks z, z + split, z + 2 split, ...
+    // of K (its waves one 32-deep round of each block), so all workgroups stream
+    // through the same moving window of B's rows rather than split separate regions.
+    const int rounds = int((p.K + int64_t(CHUNK_ALIGN) * split - 1) / (int64_t(CHUNK_ALIGN) * split));
     const uint16_t *A = static_cast<const uint16_t *>(p.A);
     const uint16_t *B = static_cast<const uint16_t *>(p.B) + n0;
-    // k of round j of this wave: k_begin + ROUND * (wave + 4 j); kround is that
-    // offset relative to k_begin.
+    // k of round j of this wave: ROUND * (wave + 4 (z + split j)).
     b_off = uint32_t((int64_t(8 * g) * p.ldb + 8 * q) * 2);
     b_row = uint32_t(p.ldb * 2);
-    const int64_t span = k_end - k_begin;           // k-rows in the chunk
-    b_klim = n0 + 8 * q < p.N ? int(span - 8 * g) : -(1 << 30);
+    b_klim = n0 + 8 * q < p.N ? int(p.K - 8 * g) : -(1 << 30);
     a_off = uint32_t((int64_t(q) * p.lda + 8 * g) * 2);
-    a_klim = q < p.M ? int(span - 8 * g) : -(1 << 30);
+    a_klim = q < p.M ? int(p.K - 8 * g) : -(1 << 30);
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = f32x4{};
 
-    const uint16_t *Ak = A + k_begin, *Bk = B + k_begin * p.ldb;
-    auto kr_of = [&](int j) { return int64_t(ROUND) * (wave + 4 * j); };
-    load<0>(Ak, Bk, kr_of(0), int(kr_of(0)));
-    load<1>(Ak, Bk, kr_of(1), int(kr_of(1)));
-    // Rounds past the chunk load zeros, so the loop needs no branches inside.
+    auto kr_of = [&](int j) { return int64_t(ROUND) * (wave + 4 * (z + int64_t(split) * j)); };
+    load<0>(A, B, kr_of(0), int(kr_of(0)));
+    load<1>(A, B, kr_of(1), int(kr_of(1)));
+    // Rounds past K load zeros, so the loop needs no branches inside.
     int j = 0;
     for (; j + 1 < rounds; j += 2) {
       multiply<0>();
-      load<0>(Ak, Bk, kr_of(j + 2), int(kr_of(j + 2)));
+      load<0>(A, B, kr_of(j + 2), int(kr_of(j + 2)));
       multiply<1>();
-      load<1>(Ak, Bk, kr_of(j + 3), int(kr_of(j + 3)));
+      load<1>(A, B, kr_of(j + 3), int(kr_of(j + 3)));
     }
     if (j < rounds) multiply<0>();
-    // The loads still in flight read zeros past the chunk; let them land before the
+    // The loads still in flight read zeros past K; let them land before the
     // registers are reused by the epilogue.
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 
