@@ -41,6 +41,7 @@ const Variant kCatalogue[] = {
     {{GEMM_KIND_MFMA, 128, 128, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_128x128_W4, 4, 4, L_MFMA_128x128},
     {{GEMM_KIND_MFMA, 128, 128, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_128x128, 4, 4, -1},
     {{GEMM_KIND_MFMA, 256, 128, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_256x128, 8, 4, -1},
+    {{GEMM_KIND_MFMA, 256, 256, 32, 2, 4, 5, 1}, 512, kHalf, L_W8_256, 8, 4, L_MFMA_256x256},
     {{GEMM_KIND_MFMA, 256, 256, 64, 2, 2, 2, 1}, 256, kHalf, L_BIG_256, 8, 8, L_MFMA_256x256},
     {{GEMM_KIND_MFMA, 256, 256, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_256x256_W4, 8, 8, L_MFMA_256x256},
     {{GEMM_KIND_MFMA, 256, 256, 32, 2, 4, 4, 1}, 512, kHalf, L_RING_256x256_W8, 8, 4, L_MFMA_256x256},
@@ -71,6 +72,7 @@ double best_intensity(int elem, unsigned mask) {
 // MFMA: 4 fp32 per 16x16 block + fragments + staged 16-byte chunks.
 int regs_estimate(const Variant &v) {
   if (v.launcher == L_BIG_256) return 512;   // one wave per SIMD: 256 accumulators in AGPRs
+  if (v.launcher == L_W8_256) return 256;    // two waves per SIMD: 128 accumulators each
   if (v.launcher == L_SKINNY) return 128;    // 8 accumulators, two staged rounds, transposes
   if (is_ring(v.launcher)) {   // accumulators + two fragment sets + addressing
     return v.tm * v.tn * 4 + 2 * (v.tm + v.tn) * 4 + 24;
@@ -205,7 +207,9 @@ bool ring_shape_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bo
   return a_span < (int64_t(1) << 31) && b_span < (int64_t(1) << 31);
 }
 
-bool needs_aligned_staging(int launcher) { return is_ring(launcher) || launcher == L_BIG_256; }
+bool needs_aligned_staging(int launcher) {
+  return is_ring(launcher) || launcher == L_BIG_256 || launcher == L_W8_256;
+}
 
 bool skinny_shape_ok(const PlanData &p, std::string *why) {
   const char *msg = nullptr;

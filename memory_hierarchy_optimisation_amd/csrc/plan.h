@@ -25,6 +25,7 @@ enum LauncherId {
   L_RING_128x128_W4,
   L_BIG_256,
   L_SKINNY,
+  L_W8_256,
   L_COUNT
 };
 
