@@ -1,21 +1,25 @@
 // kernels_w8.hip -- fp16 / bf16 GEMM for large aligned problems: 256 x 256 workgroup
-// tiles, eight waves (two per SIMD) of 128 x 64 register tiles, both operands loaded
-// straight into a five-slot LDS ring of 32-deep K slabs.
+// tiles, eight waves (two per SIMD) of 128 x 64 register tiles in a ping-pong
+// schedule, both operands loaded straight into a five-slot LDS ring of 32-deep slabs.
 //
 // The three tiling levels of "Tiling 策略与内存层次优化" (multi-level tiling) sized for
 // gfx950:
 //   * workgroup tile 256 x 256: tile intensity 2*256*256 / (512*2) = 128 FLOP/B (same
 //     page, how tiling raises intensity), one tile per compute unit at 4096^2;
 //   * K slabs of 32 in a ring of five 32 KiB LDS slots (160 KB, constraint 1 of the
-//     same page with stages = 5): three slabs in flight while one is consumed (N-stage
-//     pipelining, double-buffering section), loaded with 16-byte LDS-destination
-//     buffer loads, the gfx950 counterpart of cp.async (cp.async section);
+//     same page with stages = 5), loaded about four slabs ahead with 16-byte
+//     LDS-destination buffer loads, the gfx950 counterpart of cp.async (cp.async
+//     section);
 //   * eight waves, two per SIMD, each owning 128 x 64 of C as 4 x 2 accumulators of
-//     32 x 32 (v_mfma_f32_32x32x16_{bf16,f16}; 128 fp32 registers a lane).  With one
-//     wave per SIMD the wave stalls on its own global and LDS instructions and the
-//     matrix pipe idles meanwhile; with two, the other wave's matrix instructions
-//     issue in those gaps, so a register tile of half the size ("寄存器Tiling", 1.3:
-//     the register budget trades tile size for resident waves) pays for itself.
+//     32 x 32 (v_mfma_f32_32x32x16_{bf16,f16}; 128 fp32 registers a lane).
+// Ping-pong: the waves form two groups, one wave of each per SIMD (waves 0-3 own rows
+// 0-127 of the tile, waves 4-7 rows 128-255).  Block barriers cut time into phases; in
+// each phase one group runs the 16 matrix instructions of a slab back to back, with no
+// memory instruction among them, while the other group reads its fragments of the next
+// slab from LDS and issues one operand's loads for a slab four ahead.  A wave that
+// interleaves its own loads with its matrix instructions stalls at them, and a SIMD
+// whose two waves do the same thing at the same time stalls with them; here the
+// matrix pipe of every SIMD is fed by one wave while the other waits on memory.
 // Operands are stored in LDS in their global orientation:
 //   * a K-contiguous operand (row-major A, column-major B) as 256 rows of 64 bytes;
 //     each fragment is one 16-byte LDS read per lane;
@@ -42,8 +46,9 @@ constexpr int BM = 256, BN = 256, BK = 32, NT = 512, SLOTS = 5;
 constexpr int OP_BYTES = 256 * BK * 2;          // one operand's slab: 16 KiB
 constexpr int SLOT_BYTES = 2 * OP_BYTES;        // A at +0, B at +16 KiB
 constexpr int WTM = 128, WTN = 64;              // register tile of a wave
-constexpr int LOADS = OP_BYTES / (NT * 16);     // 16-byte loads per lane per operand and slab (2)
-constexpr int PER_SLAB = 2 * LOADS;             // loads per lane and slab, both operands
+constexpr int GROUP = 4;                        // waves of a group (one per SIMD)
+constexpr int LOADS = OP_BYTES / (GROUP * 64 * 16);   // 16-byte loads per lane of a slab's operand (4)
+constexpr int AHEAD = 4;                        // slab t+4 is requested while slab t is read
 constexpr uint32_t kOut = 0x80000000u;          // beyond every buffer range: loads zeros
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
@@ -67,20 +72,24 @@ __device__ __forceinline__ u32x2 lds_ld_tr(uint32_t a) {
 __device__ __forceinline__ uint32_t kc_off(int r, int c) { return uint32_t(r * 64 + 16 * (c ^ ((r >> 2) & 3))); }
 __device__ __forceinline__ uint32_t mn_off(int k, int c) { return uint32_t(k * 512 + 16 * (c ^ (4 * (k & 3)))); }
 
-// One operand: its slab loads and its fragment reads.
-template <bool KC>
-struct Operand {
+// The slab loads of one wave.  Each group loads one operand: group 0 A, group 1 B.
+// The four waves of a group fill an operand's 16 KiB slab: load j of group wave w
+// fills LDS bytes (4 j + w) * 1024 .. +1023 of it; lane l writes chunk slot
+// (4 j + w) * 64 + l and loads the chunk that belongs there.
+struct Loader {
   uint32_t off[LOADS];   // byte offset of the lane's chunk from the slab origin, per load
   int kin[LOADS];        // k of the chunk within the slab; 2^30 when its rows (m or n)
                          // lie outside the matrix, so that it is never loaded
-  int64_t ld;
-  // Load j of wave w fills LDS bytes (8 j + w) * 1024 .. +1023 of the slab; lane l
-  // writes chunk slot (8 j + w) * 64 + l and loads the chunk that belongs there.
-  __device__ __forceinline__ void init(int64_t ld_, int mn0, int64_t MN, int wave, int lane) {
-    ld = ld_;
+  const uint16_t *origin0;   // slab origin at k = 0 (wave-uniform)
+  int64_t kstep;             // elements between the origins of consecutive k (1 or ld)
+  uint32_t lds_off;          // the operand's area in a slot (0: A, OP_BYTES: B)
+  // KC: the operand is K-contiguous (rows of m or n with k inside), else M/N-contiguous.
+  template <bool KC>
+  __device__ __forceinline__ void init(const uint16_t *g, int64_t ld, int mn0, int64_t MN, int wave, int lane,
+                                       uint32_t area) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int slot = (8 * j + wave) * 64 + lane;
+      const int slot = (GROUP * j + wave) * 64 + lane;
       if (KC) {
         const int r = slot >> 2, c = (slot & 3) ^ ((r >> 2) & 3);
         off[j] = uint32_t((int64_t(r) * ld + 8 * c) * 2);
@@ -91,17 +100,17 @@ struct Operand {
         kin[j] = mn0 + 8 * c < MN ? k : 1 << 30;
       }
     }
+    origin0 = KC ? g + int64_t(mn0) * ld : g + mn0;
+    kstep = KC ? 1 : ld;
+    lds_off = area;
   }
-  __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const uint16_t *g, int mn0, int k0) const {
-    return rsrc_of(KC ? g + int64_t(mn0) * ld + k0 : g + int64_t(k0) * ld + mn0);
-  }
-  // Load j of the slab at k0 into the operand's LDS area `dst` (wave-uniform; so is
-  // `wave`: the LDS destination of these loads is a scalar register).
-  __device__ __forceinline__ void issue(__amdgpu_buffer_rsrc_t rs, int k_left, uint32_t dst, uint32_t wave,
-                                        int j) const {
+  // Load j of the slab at k0 into `slot` (wave-uniform; so is `wave`, the wave's index
+  // in its group: the LDS destination of these loads is a scalar register).
+  __device__ __forceinline__ void issue(int k0, int k_left, uint32_t slot, uint32_t wave, int j) const {
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(origin0 + k0 * kstep);
     const bool in = kin[j] < k_left;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MHG_LDS void *)(size_t)(dst + (8 * j + wave) * 1024), 16,
-                                             in ? off[j] : kOut, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MHG_LDS void *)(size_t)(slot + lds_off + (GROUP * j + wave) * 1024),
+                                             16, in ? off[j] : kOut, 0, 0, 0);
   }
 };
 
@@ -158,127 +167,91 @@ struct W8Gemm {
   const uint16_t *A, *B;
   int m0, n0;
   int kdim;                   // K (below 2^31 by the plan's validation)
-  uint32_t lds0, wave;
-  Operand<A_KC> oa;
-  Operand<B_KC> ob;
+  uint32_t lds0;
+  uint32_t grp, gw;           // group (0: waves 0-3, 1: waves 4-7), wave within the group
+  Loader ld;                  // group 0 loads A, group 1 loads B
   // Lane offsets of the fragment reads within an operand slab (step 0), the wave's
   // block offset included: K-contiguous operands use [0] (step 1 is [0] ^ 32, the
   // wave's block i adds 2048 i); M/N-contiguous ones one per block (step 1 adds 8192,
   // the high k-half 2048).
   uint32_t fa_off[4], fb_off[2];
   f32x16 acc[4][2];
-  // Fragment sets (step s of a slab uses set s), as low and high halves (k 0..3 and
-  // 4..7 of the lane's eight): a 16-byte read fills both, a transpose read one.
+  // The fragments of one slab, [step][block][half] (k 0..3 and 4..7 of the lane's
+  // eight): a 16-byte read fills both halves, a transpose read one.
   u32x2 fa[2][4][2], fb[2][2][2];
 
-  // Reads of one step, in the order the next step needs them: B block 0, A block 0,
-  // B block 1, A blocks 1..3; a fragment is one read (K-contiguous) or two.
   static constexpr int NA = A_KC ? 1 : 2, NB = B_KC ? 1 : 2;
-  static constexpr int T = 2 * NB + 4 * NA;          // reads per step
-  // Fragment (0..3: A block, 4..5: B block) and half of read k.
+  static constexpr int T = 2 * NB + 4 * NA;          // LDS reads per step
+
+  __device__ __forceinline__ W8Gemm(const LaunchArgs &p_) : p(p_) {}
+
+  // Read k of step S (B block 0, A block 0, B block 1, A blocks 1..3; a fragment is one
+  // read if K-contiguous, two if M/N-contiguous) from the slab whose A area is `slot`.
   static constexpr int read_frag(int k) {
     return k < NB ? 4 : k < NB + NA ? 0 : k < 2 * NB + NA ? 5 : 1 + (k - 2 * NB - NA) / NA;
   }
   static constexpr int read_half(int k) {
     return k < NB ? k : k < NB + NA ? k - NB : k < 2 * NB + NA ? k - NB - NA : (k - 2 * NB - NA) % NA;
   }
-  // Reads the matrix instruction m of a step needs, counted from the first.
-  static constexpr int needed(int m) {
-    return m == 0 ? NB + NA : m == 1 ? 2 * NB + NA : m < 4 ? 2 * NB + 2 * NA : m < 6 ? 2 * NB + 3 * NA : T;
-  }
-  // Reads issued after matrix instruction n of a step: [first(n), first(n + 1)).
-  static constexpr int first(int n) { return n * T / 8; }
-  // LDS operations that may still be outstanding when matrix instruction m starts:
-  // the previous step's reads after the ones it needs, and this step's reads so far.
-  static constexpr int allowed(int m) {
-    return (T - needed(m) + first(m)) < 15 ? T - needed(m) + first(m) : 15;
-  }
-
-  __device__ __forceinline__ W8Gemm(const LaunchArgs &p_) : p(p_) {}
-
-  // Read k of step S into set SET from the slab whose A area starts at `slot`.
-  template <int SET, int S, int K>
+  template <int S, int K>
   __device__ __forceinline__ void read(uint32_t slot) {
     constexpr int f = read_frag(K), h = read_half(K);
     if constexpr (f < 4) {
       if constexpr (A_KC) {
-        ds_b128<2048 * f>(*reinterpret_cast<u32x4 *>(&fa[SET][f][0]), slot + (fa_off[0] ^ uint32_t(32 * S)));
+        ds_b128<2048 * f>(*reinterpret_cast<u32x4 *>(&fa[S][f][0]), slot + (fa_off[0] ^ uint32_t(32 * S)));
       } else {
-        ds_tr<8192 * S + 2048 * h>(fa[SET][f][h], slot + fa_off[f]);
+        ds_tr<8192 * S + 2048 * h>(fa[S][f][h], slot + fa_off[f]);
       }
     } else {
       constexpr int j = f - 4;
       if constexpr (B_KC) {
-        ds_b128<OP_BYTES + 2048 * j>(*reinterpret_cast<u32x4 *>(&fb[SET][j][0]), slot + (fb_off[0] ^ uint32_t(32 * S)));
+        ds_b128<OP_BYTES + 2048 * j>(*reinterpret_cast<u32x4 *>(&fb[S][j][0]), slot + (fb_off[0] ^ uint32_t(32 * S)));
       } else {
-        ds_tr<OP_BYTES + 8192 * S + 2048 * h>(fb[SET][j][h], slot + fb_off[j]);
+        ds_tr<OP_BYTES + 8192 * S + 2048 * h>(fb[S][j][h], slot + fb_off[j]);
       }
     }
   }
-  // Reads first(n) .. first(n + 1) - 1.
-  template <int SET, int S, int N>
-  __device__ __forceinline__ void reads_after(uint32_t slot) {
-    if constexpr (first(N) < first(N + 1)) { read<SET, S, first(N)>(slot); MHG_ORDER(); }
-    if constexpr (first(N) + 1 < first(N + 1)) { read<SET, S, first(N) + 1>(slot); MHG_ORDER(); }
+  // Reads K .. T-1 of step S; the group's two loads of the step go after reads 1 and
+  // T / 2 + 1 (T >= 6, so both exist).
+  template <int S, int K>
+  __device__ __forceinline__ void reads_from(uint32_t slot, int t) {
+    if constexpr (K < T) {
+      read<S, K>(slot); MHG_ORDER();
+      if constexpr (K == 1 || K == T / 2 + 1) { issue(t + AHEAD, 2 * S + (K != 1)); MHG_ORDER(); }
+      reads_from<S, K + 1>(slot, t);
+    }
   }
-  // Matrix instruction m of a step on set SET (accumulator (m / 2, m % 2)), after the
-  // wait for the fragments it needs.
-  template <int SET, int M>
-  __device__ __forceinline__ void mma() {
-    if constexpr (M == 0 || M == 1 || M == 2 || M == 4 || M == 6) { wait_lgkm<allowed(M)>(); MHG_ORDER(); }
-    constexpr int i = M >> 1, j = M & 1;
-    const u32x4 a = {fa[SET][i][0].x, fa[SET][i][0].y, fa[SET][i][1].x, fa[SET][i][1].y};
-    const u32x4 b = {fb[SET][j][0].x, fb[SET][j][0].y, fb[SET][j][1].x, fb[SET][j][1].y};
-    acc[i][j] = mfma32(H{}, b, a, acc[i][j]);
+  // Load j (of 4) of slab t for this wave's group: A for group 0, B for group 1.
+  __device__ __forceinline__ void issue(int t, int j) const {
+    const int k0 = t * BK;
+    ld.issue(k0, kdim - k0, slot_addr(t), gw, j);
+  }
+
+  // Memory phase for slab t: read all of the wave's fragments of slab t and request
+  // its group's operand of slab t+4 (into the slot of slab t-1, which both groups have
+  // finished reading: the last reader ended its phase with every read complete).
+  __device__ __forceinline__ void mem(int t) {
+    const uint32_t slot = slot_addr(t);
+    reads_from<0, 0>(slot, t);
+    reads_from<1, 0>(slot, t);
+    wait_lgkm<0>();
+    MHG_ORDER();
+  }
+  // Compute phase: the 16 matrix instructions of a slab, back to back.
+  __device__ __forceinline__ void compute() {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int i = m >> 1, j = m & 1;
+        const u32x4 a = {fa[s][i][0].x, fa[s][i][0].y, fa[s][i][1].x, fa[s][i][1].y};
+        const u32x4 b = {fb[s][j][0].x, fb[s][j][0].y, fb[s][j][1].x, fb[s][j][1].y};
+        acc[i][j] = mfma32(H{}, b, a, acc[i][j]);
+        MHG_ORDER();
+      }
   }
 
   __device__ __forceinline__ uint32_t slot_addr(int t) const { return lds0 + uint32_t(t % SLOTS) * SLOT_BYTES; }
-  __device__ __forceinline__ void issue_a(int t, int j) const {
-    const int k0 = t * BK;
-    oa.issue(oa.rsrc(A, m0, k0), kdim - k0, slot_addr(t), wave, j);
-  }
-  __device__ __forceinline__ void issue_b(int t, int j) const {
-    const int k0 = t * BK;
-    ob.issue(ob.rsrc(B, n0, k0), kdim - k0, slot_addr(t) + OP_BYTES, wave, j);
-  }
-
-  // Step S of slab t: matrix instructions on set S; after instruction n the next
-  // step's reads first(n) .. (into the other set, from slot `rd`), and loads at n = 1
-  // and n = 5 (`S == 0`: B of slab t+3, else A of slab t+4).
-  template <int S, int N>
-  __device__ __forceinline__ void step_from(int t, uint32_t rd) {
-    if constexpr (N < 8) {
-      mma<S, N>(); MHG_ORDER();
-      reads_after<S ^ 1, S ^ 1, N>(rd);
-      if constexpr (N == 1 || N == 5) {
-        if constexpr (S == 0) issue_b(t + 3, N >> 2);
-        else issue_a(t + 4, N >> 2);
-        MHG_ORDER();
-      }
-      step_from<S, N + 1>(t, rd);
-    }
-  }
-
-  template <int K>
-  __device__ __forceinline__ void prologue_reads(uint32_t slot) {
-    if constexpr (K < T) { read<0, 0, K>(slot); MHG_ORDER(); prologue_reads<K + 1>(slot); }
-  }
-
-  // One 32-deep slab t in two 16-deep steps of 8 matrix instructions.
-  //   step 0: multiply set 0 (step 0 of slab t); read step 1 of slab t into set 1;
-  //           load B of slab t+3 (its slot held slab t-2, free since the last barrier).
-  //   wait for this wave's loads of slab t+1, barrier: slab t+1 is in LDS and every
-  //           wave has finished reading slab t-1.
-  //   step 1: multiply set 1; read step 0 of slab t+1 into set 0; load A of slab t+4
-  //           into the slot of slab t-1.
-  // Loads in flight per wave after the wait: slab t+2 and slab t+3 (four each).
-  __device__ __forceinline__ void slab(int t) {
-    step_from<0, 0>(t, slot_addr(t));
-    wait_vm<2 * PER_SLAB>();
-    barrier();
-    MHG_ORDER();
-    step_from<1, 0>(t, slot_addr(t + 1));
-  }
 
   __device__ __forceinline__ void run(uint32_t lds_base) {
     int tm, tn;
@@ -287,12 +260,14 @@ struct W8Gemm {
     n0 = tn * BN;
     lds0 = lds_base;
     const int lane = threadIdx.x & 63;
-    wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    grp = wave >> 2;
+    gw = wave & 3;
     const int wm = wave >> 2, wn = wave & 3;
     A = static_cast<const uint16_t *>(p.A);
     B = static_cast<const uint16_t *>(p.B);
-    oa.init(p.lda, m0, p.M, wave, lane);
-    ob.init(p.ldb, n0, p.N, wave, lane);
+    if (grp == 0) ld.init<A_KC>(A, p.lda, m0, p.M, gw, lane, 0);
+    else ld.init<B_KC>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
     if (A_KC) {
       fa_off[0] = kc_lane(lane) + 2048 * 4 * wm;     // row blocks 4 wm .. 4 wm + 3
     } else {
@@ -312,30 +287,98 @@ struct W8Gemm {
     kdim = int(p.K);
     const int KT = (kdim + BK - 1) / BK;
 
-    // Prologue: slabs 0..2 and A of slab 3 requested (B of slab 3 goes out in slab 0's
-    // first step, as in every later slab), in the order the loop's waits assume.
-    for (int t = 0; t < 3; ++t) {
-      issue_a(t, 0); issue_a(t, 1); issue_b(t, 0); issue_b(t, 1);
-    }
-    issue_a(3, 0); issue_a(3, 1);
-    wait_vm<2 * PER_SLAB + LOADS>();   // slab 0 landed (younger: slabs 1, 2, A of 3)
-    wait_lgkm<0>();                    // nothing else counts against lgkmcnt below
+    // Every wave runs the same loop, mem(t); barrier; compute(); barrier, but group 1
+    // passes one extra barrier before it and group 0 one after it, so group 1 runs one
+    // phase behind: in phase 2t group 0 reads slab t while group 1 multiplies slab t-1,
+    // in phase 2t+1 group 0 multiplies slab t while group 1 reads it.  Group 0 requests
+    // A of slab t+4 in phase 2t, group 1 B of slab t+4 in phase 2t+1; slab t+1 must be
+    // in LDS when phase 2t+2 starts, so before every barrier each wave waits until at
+    // most its three younger slabs' loads (12) are in flight.
+    wait_lgkm<0>();                     // nothing else counts against lgkmcnt below
+#pragma unroll
+    for (int t = 0; t < AHEAD; ++t)
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) issue(t, j);
+    wait_vm<3 * LOADS>();               // slab 0 landed
     barrier();
+    if (grp == 1) barrier();
     MHG_ORDER();
-    prologue_reads<0>(slot_addr(0));
-
-    for (int t = 0; t < KT; ++t) slab(t);
+    for (int t = 0; t < KT; ++t) {
+      mem(t);
+      wait_vm<3 * LOADS>();
+      barrier();
+      MHG_ORDER();
+      compute();
+      wait_vm<3 * LOADS>();
+      barrier();
+      MHG_ORDER();
+    }
+    if (grp == 0) barrier();
     // Loads past K (zeros) are still writing LDS: drain them before the workgroup ends.
-    // The last step's fragment reads are never consumed; the compiler does not know
-    // they are in flight, so they must land before their registers are reused.
     wait_vm<0>();
-    wait_lgkm<0>();
     MHG_ORDER();
 
     // acc[i][j] holds the transposed 32 x 32 block: element r of lane l is
-    // C[row m0 + 128 wm + 32 i + l % 32][col n0 + 64 wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4].
-    const int64_t row0 = m0 + wm * WTM + (lane & 31);
-    const int64_t colL = n0 + wn * WTN + 4 * (lane >> 5);
+    // C[row 128 wm + 32 i + l % 32][col 64 wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of
+    // the tile.  A lane's four consecutive columns are a 16-byte piece of one row, and a
+    // store instruction would touch 32 rows; staged through LDS instead, every store
+    // writes whole 128-byte (16-bit C) or 256-byte (fp32 C) row segments.
+    const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
+    const int ob = p.out_code == E_F32 ? 4 : 2;
+    const bool c16 = ((uintptr_t(p.C) | uintptr_t(p.ldc * ob)) & 15) == 0;
+    if (c16) {
+      barrier();                        // every wave is done with the ring
+      const uint32_t region = lds0 + wave * 16384;
+      if (p.out_code == E_F32) {
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+          // rows 64 pass .. +63 of the wave's block, 256 bytes a row; chunk c of row r
+          // at 16 (c ^ (r % 16)): sixteen rows written at one chunk hit 16 bank groups
+#pragma unroll
+          for (int i2 = 0; i2 < 2; ++i2)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int i = 2 * pass + i2, r = 32 * i2 + (lane & 31), c = 8 * j + 2 * q + (lane >> 5);
+                const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+                *reinterpret_cast<MHG_LDS f32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15)))) = v;
+              }
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const int r = 4 * k + (lane >> 4), c = lane & 15;
+            const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15))));
+            store_chunk(rowW + 64 * pass + r, colW + 4 * c, v, 4);
+          }
+        }
+      } else {
+        // 128 bytes a row; chunk c of row r at 16 (c ^ ((r / 2) % 8))
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 32 * i + (lane & 31), c = 4 * j + q;
+              uint16_t h[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                h[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][4 * q + e])
+                                           : __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][4 * q + e]);
+              const u32x2 v = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+              *reinterpret_cast<MHG_LDS u32x2 *>(size_t(region + r * 128 + 16 * (c ^ ((r >> 1) & 7)) + 8 * (lane >> 5))) = v;
+            }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int r = 8 * k + (lane >> 3), c = lane & 7;
+          const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 128 + 16 * (c ^ ((r >> 1) & 7))));
+          store_chunk(rowW + r, colW + 8 * c, v, 8);
+        }
+      }
+      return;
+    }
+    const int64_t row0 = rowW + (lane & 31);
+    const int64_t colL = colW + 4 * (lane >> 5);
     const bool c_vec = p.c_vec != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -351,6 +394,25 @@ struct W8Gemm {
           const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
           store_out4(p.C, row * p.ldc + col, v, p.out_code, c_vec && n_in >= 4, int(n_in));
         }
+    }
+  }
+
+  // 16 bytes of converted output (W elements) for C[row][col .. col + W - 1]: one
+  // store when all W lie inside the matrix, else the elements that do.
+  __device__ __forceinline__ void store_chunk(int64_t row, int64_t col, u32x4 v, int W) const {
+    if (row >= p.M || col >= p.N) return;
+    const int64_t idx = row * p.ldc + col;
+    if (col + W <= p.N) {
+      if (W == 4) *reinterpret_cast<u32x4 *>(static_cast<float *>(p.C) + idx) = v;
+      else *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p.C) + idx) = v;
+      return;
+    }
+    const int n_in = int(p.N - col);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e >= W || e >= n_in) break;
+      if (W == 4) static_cast<uint32_t *>(p.C)[idx + e] = v[e];
+      else static_cast<uint16_t *>(p.C)[idx + e] = uint16_t(v[e >> 1] >> (16 * (e & 1)));
     }
   }
 };
