@@ -21,7 +21,7 @@ hipError_t launch_fill(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_ring(int launcher, const LaunchArgs &p, hipStream_t s);
 bool ring_supported(const LaunchArgs &p, int bm, int bn);
 hipError_t launch_big(const LaunchArgs &p, hipStream_t s);
-hipError_t launch_w8(const LaunchArgs &p, hipStream_t s);
+hipError_t launch_w8(const LaunchArgs &p, int bm, hipStream_t s);
 hipError_t launch_skinny(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_zero_words(void *w, int64_t n, hipStream_t s);
 }  // namespace mhg
@@ -208,8 +208,8 @@ int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stre
         e = mhg::launch_ring(v->launcher, a, s); break;
       case mhg::L_BIG_256:
         e = mhg::launch_big(a, s); break;
-      case mhg::L_W8_256:
-        e = mhg::launch_w8(a, s); break;
+      case mhg::L_W8_256: case mhg::L_W8_128:
+        e = mhg::launch_w8(a, v->cfg.bm, s); break;
       case mhg::L_SKINNY:
         e = mhg::launch_skinny(a, s); break;
       default:

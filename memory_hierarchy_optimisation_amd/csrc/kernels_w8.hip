@@ -1,30 +1,37 @@
-// kernels_w8.hip -- fp16 / bf16 GEMM for large aligned problems: 256 x 256 workgroup
-// tiles, eight waves (two per SIMD) of 128 x 64 register tiles in a ping-pong
-// schedule, both operands loaded straight into a five-slot LDS ring of 32-deep slabs.
+// kernels_w8.hip -- fp16 / bf16 GEMM for large aligned problems: eight waves (two per
+// SIMD) in a ping-pong schedule, both operands loaded straight into a five-slot LDS
+// ring of K slabs.  Two tile shapes:
+//   * 256 x 256, 32-deep slabs: the two wave groups split the tile's rows, each wave
+//     owns 128 x 64 of C (4 x 2 accumulators of 32 x 32);
+//   * 128 x 128, 64-deep slabs: the two wave groups split each slab's K (first and
+//     second 32), each wave owns 64 x 64 of C (2 x 2 accumulators), and the two
+//     partial sums of a block are added through LDS at the end.
+// Both slabs are 32 KiB (16 KiB of A at +0, 16 KiB of B at +16 KiB), so both shapes
+// use the same ring: five slots, 160 KB.
 //
 // The three tiling levels of "Tiling 策略与内存层次优化" (multi-level tiling) sized for
 // gfx950:
-//   * workgroup tile 256 x 256: tile intensity 2*256*256 / (512*2) = 128 FLOP/B (same
-//     page, how tiling raises intensity), one tile per compute unit at 4096^2;
-//   * K slabs of 32 in a ring of five 32 KiB LDS slots (160 KB, constraint 1 of the
-//     same page with stages = 5), loaded about four slabs ahead with 16-byte
-//     LDS-destination buffer loads, the gfx950 counterpart of cp.async (cp.async
-//     section);
-//   * eight waves, two per SIMD, each owning 128 x 64 of C as 4 x 2 accumulators of
-//     32 x 32 (v_mfma_f32_32x32x16_{bf16,f16}; 128 fp32 registers a lane).
-// Ping-pong: the waves form two groups, one wave of each per SIMD (waves 0-3 own rows
-// 0-127 of the tile, waves 4-7 rows 128-255).  Block barriers cut time into phases; in
-// each phase one group runs the 16 matrix instructions of a slab back to back, with no
-// memory instruction among them, while the other group reads its fragments of the next
-// slab from LDS and issues one operand's loads for a slab four ahead.  A wave that
-// interleaves its own loads with its matrix instructions stalls at them, and a SIMD
-// whose two waves do the same thing at the same time stalls with them; here the
+//   * workgroup tile: 256 x 256 has tile intensity 2*256*256 / (512*2) = 128 FLOP/B
+//     (same page, how tiling raises intensity) and covers 4096^2 with one tile per
+//     compute unit; 128 x 128 (64 FLOP/B) covers 2048^2 the same way;
+//   * K slabs in a ring of five 32 KiB LDS slots (constraint 1 of the same page with
+//     stages = 5), requested four slabs ahead with 16-byte LDS-destination buffer
+//     loads, the gfx950 counterpart of cp.async (cp.async section);
+//   * eight waves, two per SIMD, each with a 32 x 32 accumulator tile per
+//     v_mfma_f32_32x32x16_{bf16,f16} ("寄存器Tiling", 1.3: the register budget trades
+//     tile size for resident waves; 128 or 64 fp32 accumulators a lane).
+// Ping-pong: the waves form two groups, one wave of each per SIMD.  Block barriers
+// cut time into phases; in each phase one group runs the matrix instructions of a
+// slab back to back, with no memory instruction among them, while the other group
+// reads its fragments of the next slab from LDS and issues one operand's loads.  A
+// wave that interleaves its own loads with its matrix instructions stalls at them, and
+// a SIMD whose two waves do the same thing at the same time stalls with them; here the
 // matrix pipe of every SIMD is fed by one wave while the other waits on memory.
 // Operands are stored in LDS in their global orientation:
-//   * a K-contiguous operand (row-major A, column-major B) as 256 rows of 64 bytes;
-//     each fragment is one 16-byte LDS read per lane;
-//   * an M/N-contiguous operand (column-major A, row-major B) as 32 k-rows of 512
-//     bytes; each fragment is two LDS transpose reads (ds_read_b64_tr_b16), so the
+//   * a K-contiguous operand (row-major A, column-major B) as rows of BK values; each
+//     fragment is one 16-byte LDS read per lane;
+//   * an M/N-contiguous operand (column-major A, row-major B) as k-rows of the tile's
+//     width; each fragment is two LDS transpose reads (ds_read_b64_tr_b16), so the
 //     operand is never transposed in registers.
 // Both layouts XOR-swizzle 16-byte chunks (bank conflicts and swizzle section:
 // row XOR column) so that the fragment reads are conflict-free; a loaded lane's 16
@@ -35,42 +42,43 @@
 // range and arrive as zeros ("CUDA tile", 4: zero is the identity of the sum); stores
 // are masked.  The host requires 16-byte aligned operands whose contiguous extents and
 // leading dimensions are multiples of 8 elements.
-#include <type_traits>
-
 #include "device.h"
 
 namespace mhg {
 namespace w8 {
 
-constexpr int BM = 256, BN = 256, BK = 32, NT = 512, SLOTS = 5;
-constexpr int OP_BYTES = 256 * BK * 2;          // one operand's slab: 16 KiB
+constexpr int NT = 512, SLOTS = 5;
+constexpr int OP_BYTES = 16384;                 // one operand's slab (both shapes)
 constexpr int SLOT_BYTES = 2 * OP_BYTES;        // A at +0, B at +16 KiB
-constexpr int WTM = 128, WTN = 64;              // register tile of a wave
 constexpr int GROUP = 4;                        // waves of a group (one per SIMD)
 constexpr int LOADS = OP_BYTES / (GROUP * 64 * 16);   // 16-byte loads per lane of a slab's operand (4)
 constexpr int AHEAD = 4;                        // slab t+4 is requested while slab t is read
 constexpr uint32_t kOut = 0x80000000u;          // beyond every buffer range: loads zeros
 
+// The two tile shapes.  FM x FN accumulators of 32 x 32 per wave; KSPLIT = 2: the
+// groups take the first and second half of each slab's K instead of halves of the rows.
+struct Tile256 { static constexpr int BM = 256, BN = 256, BK = 32, FM = 4, FN = 2, KSPLIT = 1; };
+struct Tile128 { static constexpr int BM = 128, BN = 128, BK = 64, FM = 2, FN = 2, KSPLIT = 2; };
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
 }
 
-__device__ __forceinline__ u32x4 lds_ld(uint32_t a) {
-  return *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(a));
-}
-__device__ __forceinline__ u32x2 lds_ld_tr(uint32_t a) {
-  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((MHG_LDS bf16x4 *)(size_t)a));
-}
-
-// LDS layouts of one operand's slab (byte offsets within its 16 KiB):
-//   K-contiguous: row r (0..255) of four 16-byte k-chunks; chunk c at r*64 + 16*(c ^ ((r >> 2) & 3)).
-//     Sixteen consecutive rows read at one chunk (a fragment read, 16 lanes an LDS
-//     cycle) land on 16 distinct 16-byte bank groups.
-//   M/N-contiguous: k-row k (0..31) of 32 chunks of 8 m/n-values; chunk c at
-//     k*512 + 16*(c ^ (4*(k & 3))).  A transpose read touches four consecutive k-rows,
+// LDS layouts of one operand's slab (byte offsets within its 16 KiB), for a tile side
+// of R rows (m or n) and slabs BK deep:
+//   K-contiguous: row r (0..R-1) of BK/8 16-byte k-chunks; chunk c at
+//     r * 2BK + 16 (c ^ kswz(r)), kswz(r) = (r >> 2) & 3 for 4 chunks a row,
+//     (r >> 1) & 7 for 8.  Sixteen consecutive rows read at one chunk (a fragment read,
+//     16 lanes an LDS cycle) land on 16 distinct 16-byte bank groups.
+//   M/N-contiguous: k-row k (0..BK-1) of R/8 chunks of 8 m/n-values; chunk c at
+//     k * 2R + 16 (c ^ 4 (k & 3)).  A transpose read touches four consecutive k-rows,
 //     64 bytes each; the XOR moves them to four distinct quarters of the banks.
-__device__ __forceinline__ uint32_t kc_off(int r, int c) { return uint32_t(r * 64 + 16 * (c ^ ((r >> 2) & 3))); }
-__device__ __forceinline__ uint32_t mn_off(int k, int c) { return uint32_t(k * 512 + 16 * (c ^ (4 * (k & 3)))); }
+template <int BK>
+__device__ __forceinline__ constexpr int kswz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
+template <int BK>
+__device__ __forceinline__ uint32_t kc_off(int r, int c) { return uint32_t(r * 2 * BK + 16 * (c ^ kswz<BK>(r))); }
+template <int R>
+__device__ __forceinline__ uint32_t mn_off(int k, int c) { return uint32_t(k * 2 * R + 16 * (c ^ (4 * (k & 3)))); }
 
 // The slab loads of one wave.  Each group loads one operand: group 0 A, group 1 B.
 // The four waves of a group fill an operand's 16 KiB slab: load j of group wave w
@@ -83,19 +91,22 @@ struct Loader {
   const uint16_t *origin0;   // slab origin at k = 0 (wave-uniform)
   int64_t kstep;             // elements between the origins of consecutive k (1 or ld)
   uint32_t lds_off;          // the operand's area in a slot (0: A, OP_BYTES: B)
-  // KC: the operand is K-contiguous (rows of m or n with k inside), else M/N-contiguous.
-  template <bool KC>
+  // KC: the operand is K-contiguous (rows of m or n with k inside), else M/N-contiguous;
+  // R: the tile's extent in m or n.
+  template <bool KC, int R, int BK>
   __device__ __forceinline__ void init(const uint16_t *g, int64_t ld, int mn0, int64_t MN, int wave, int lane,
                                        uint32_t area) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
       const int slot = (GROUP * j + wave) * 64 + lane;
       if (KC) {
-        const int r = slot >> 2, c = (slot & 3) ^ ((r >> 2) & 3);
+        constexpr int CPR = BK / 8;                       // chunks a row
+        const int r = slot / CPR, c = (slot % CPR) ^ kswz<BK>(r);
         off[j] = uint32_t((int64_t(r) * ld + 8 * c) * 2);
         kin[j] = mn0 + r < MN ? 8 * c : 1 << 30;
       } else {
-        const int k = slot >> 5, c = (slot & 31) ^ (4 * (k & 3));
+        constexpr int CPK = R / 8;                        // chunks a k-row
+        const int k = slot / CPK, c = (slot % CPK) ^ (4 * (k & 3));
         off[j] = uint32_t((int64_t(k) * ld + 8 * c) * 2);
         kin[j] = mn0 + 8 * c < MN ? k : 1 << 30;
       }
@@ -116,37 +127,31 @@ struct Loader {
 
 // Fragment addressing.  A 32 x 16 fragment (32 rows of m or n, 16 k) for
 // v_mfma_f32_32x32x16: lane l holds row l % 32, k = 8 (l / 32) .. +7 of the 16-deep
-// step.
-//   K-contiguous: one 16-byte read at kc_off(b + l % 32, 2 s + l / 32).  The swizzle
-//     term depends on the lane only (b is a multiple of 32), so the step s is an XOR of
-//     32 on the lane's offset and the block b a constant 64 b.
+// step s.
+//   K-contiguous: one 16-byte read at kc_off(32 b + l % 32, 2 s + l / 32).  The swizzle
+//     term depends on the lane only (32 b leaves bits 0..4 of the row alone), and 2 s
+//     has no bit in common with l / 32 or with the swizzle's low bit, so step s is an
+//     XOR of 32 s on the lane's offset and block b a constant 32 b * 2BK.
 //   M/N-contiguous: two transpose reads (e = 0, 1) for k = 8 (l / 32) + 4 e .. +3.  In
 //     each 16-lane group g = l / 16, lane 4 q + u addresses the 8 bytes of k-row
-//     16 s + 8 (g / 2) + 4 e + q, columns b + 16 (g % 2) + 4 u .. +3, and lane t then
-//     receives column b + 16 (g % 2) + t of those four k-rows.
-__device__ __forceinline__ uint32_t kc_lane(int lane) { return kc_off(lane & 31, lane >> 5); }
-// Offset of the transpose read of block index jb (= b / 32) for k-half e = 0, step 0.
-__device__ __forceinline__ uint32_t mn_lane(int lane, int jb) {
+//     16 s + 8 (g / 2) + 4 e + q, columns 32 b + 16 (g % 2) + 4 u .. +3, and lane t then
+//     receives column 32 b + 16 (g % 2) + t of those four k-rows; step s adds 16 s * 2R
+//     and e adds 4 * 2R to the lane's offset for step 0, e = 0.
+template <int BK>
+__device__ __forceinline__ uint32_t kc_lane(int lane) { return kc_off<BK>(lane & 31, lane >> 5); }
+template <int R>
+__device__ __forceinline__ uint32_t mn_lane(int lane, int b) {
   const int g = lane >> 4, t = lane & 15, q = t >> 2, u = t & 3;
   const int k = 8 * (g >> 1) + q;
-  const int c = 4 * jb + 2 * (g & 1) + (u >> 1);
-  return mn_off(k, c) + 8 * (u & 1);
+  const int c = 4 * b + 2 * (g & 1) + (u >> 1);
+  return mn_off<R>(k, c) + 8 * (u & 1);
 }
-
-// s_waitcnt with vmcnt = n and expcnt / lgkmcnt left free.
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
-#define MHG_ORDER() __builtin_amdgcn_sched_barrier(0)
 
 // LDS reads of the fragments, issued as plain instructions.  The compiler would treat
 // a transpose read as possibly aliasing the LDS-destination loads in flight and wait
 // for all of them; the ring's waits and barriers already order those accesses, so
 // these reads are not shown to it as memory accesses, and their completion is awaited
-// explicitly (lgkmcnt) before the instruction that consumes them.
+// explicitly (lgkmcnt) before any instruction consumes them.
 template <int OFF>
 __device__ __forceinline__ void ds_b128(u32x4 &d, uint32_t a) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(d) : "v"(a), "i"(OFF));
@@ -155,59 +160,73 @@ template <int OFF>
 __device__ __forceinline__ void ds_tr(u32x2 &d, uint32_t a) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(d) : "v"(a), "i"(OFF));
 }
+// s_waitcnt with only lgkmcnt = n, or only vmcnt = n.
 template <int n>
 __device__ __forceinline__ void wait_lgkm() {
   static_assert(n >= 0 && n < 16, "lgkmcnt field");
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (n << 8));
 }
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+#define MHG_ORDER() __builtin_amdgcn_sched_barrier(0)
 
-template <class H, bool A_KC, bool B_KC>
+template <class H, bool A_KC, bool B_KC, class TL>
 struct W8Gemm {
+  static constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, FM = TL::FM, FN = TL::FN;
+  static constexpr int WTM = 32 * FM, WTN = 32 * FN;      // a wave's block of C
+  static_assert(BM * BK * 2 == OP_BYTES && BN * BK * 2 == OP_BYTES, "slab size");
+
   const LaunchArgs &p;
-  const uint16_t *A, *B;
   int m0, n0;
   int kdim;                   // K (below 2^31 by the plan's validation)
   uint32_t lds0;
   uint32_t grp, gw;           // group (0: waves 0-3, 1: waves 4-7), wave within the group
+  int wm, wn;                 // the wave's block of C: rows WTM wm, columns WTN wn
+  uint32_t ks0;               // first 16-deep step of each slab the wave multiplies
   Loader ld;                  // group 0 loads A, group 1 loads B
-  // Lane offsets of the fragment reads within an operand slab (step 0), the wave's
-  // block offset included: K-contiguous operands use [0] (step 1 is [0] ^ 32, the
-  // wave's block i adds 2048 i); M/N-contiguous ones one per block (step 1 adds 8192,
-  // the high k-half 2048).
-  uint32_t fa_off[4], fb_off[2];
-  f32x16 acc[4][2];
+  // Lane offsets of the fragment reads within an operand slab (for the wave's first
+  // step), the wave's block offset included: K-contiguous operands use [0] (the second
+  // step is [0] ^ 32, block i adds 64 BK i); M/N-contiguous ones one per block.
+  uint32_t fa_off[FM], fb_off[FN];
+  f32x16 acc[FM][FN];
   // The fragments of one slab, [step][block][half] (k 0..3 and 4..7 of the lane's
   // eight): a 16-byte read fills both halves, a transpose read one.
-  u32x2 fa[2][4][2], fb[2][2][2];
+  u32x2 fa[2][FM][2], fb[2][FN][2];
 
   static constexpr int NA = A_KC ? 1 : 2, NB = B_KC ? 1 : 2;
-  static constexpr int T = 2 * NB + 4 * NA;          // LDS reads per step
+  static constexpr int T = FN * NB + FM * NA;            // LDS reads per step
 
   __device__ __forceinline__ W8Gemm(const LaunchArgs &p_) : p(p_) {}
 
-  // Read k of step S (B block 0, A block 0, B block 1, A blocks 1..3; a fragment is one
-  // read if K-contiguous, two if M/N-contiguous) from the slab whose A area is `slot`.
+  // Read k of a step, in the order the step's matrix instructions need them (B block 0,
+  // A block 0, B block 1, A blocks 1 ..); a fragment is one read if K-contiguous, two
+  // if M/N-contiguous.  Returns the fragment (0 .. FM-1: A block, FM ..: B block).
   static constexpr int read_frag(int k) {
-    return k < NB ? 4 : k < NB + NA ? 0 : k < 2 * NB + NA ? 5 : 1 + (k - 2 * NB - NA) / NA;
+    return k < NB ? FM : k < NB + NA ? 0 : k < 2 * NB + NA ? FM + 1 : 1 + (k - 2 * NB - NA) / NA;
   }
   static constexpr int read_half(int k) {
     return k < NB ? k : k < NB + NA ? k - NB : k < 2 * NB + NA ? k - NB - NA : (k - 2 * NB - NA) % NA;
   }
+  // Read k of the wave's step S (0 or 1) from the slab whose A area is `slot`.
   template <int S, int K>
   __device__ __forceinline__ void read(uint32_t slot) {
     constexpr int f = read_frag(K), h = read_half(K);
-    if constexpr (f < 4) {
+    if constexpr (f < FM) {
       if constexpr (A_KC) {
-        ds_b128<2048 * f>(*reinterpret_cast<u32x4 *>(&fa[S][f][0]), slot + (fa_off[0] ^ uint32_t(32 * S)));
+        ds_b128<64 * BK * f>(*reinterpret_cast<u32x4 *>(&fa[S][f][0]), slot + (fa_off[0] ^ uint32_t(32 * S)));
       } else {
-        ds_tr<8192 * S + 2048 * h>(fa[S][f][h], slot + fa_off[f]);
+        ds_tr<16 * S * 2 * BM + 4 * 2 * BM * h>(fa[S][f][h], slot + fa_off[f]);
       }
     } else {
-      constexpr int j = f - 4;
+      constexpr int j = f - FM;
       if constexpr (B_KC) {
-        ds_b128<OP_BYTES + 2048 * j>(*reinterpret_cast<u32x4 *>(&fb[S][j][0]), slot + (fb_off[0] ^ uint32_t(32 * S)));
+        ds_b128<OP_BYTES + 64 * BK * j>(*reinterpret_cast<u32x4 *>(&fb[S][j][0]), slot + (fb_off[0] ^ uint32_t(32 * S)));
       } else {
-        ds_tr<OP_BYTES + 8192 * S + 2048 * h>(fb[S][j][h], slot + fb_off[j]);
+        ds_tr<OP_BYTES + 16 * S * 2 * BN + 4 * 2 * BN * h>(fb[S][j][h], slot + fb_off[j]);
       }
     }
   }
@@ -237,13 +256,13 @@ struct W8Gemm {
     wait_lgkm<0>();
     MHG_ORDER();
   }
-  // Compute phase: the 16 matrix instructions of a slab, back to back.
+  // Compute phase: the wave's 2 FM FN matrix instructions of a slab, back to back.
   __device__ __forceinline__ void compute() {
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int i = m >> 1, j = m & 1;
+      for (int m = 0; m < FM * FN; ++m) {
+        const int i = m / FN, j = m % FN;
         const u32x4 a = {fa[s][i][0].x, fa[s][i][0].y, fa[s][i][1].x, fa[s][i][1].y};
         const u32x4 b = {fb[s][j][0].x, fb[s][j][0].y, fb[s][j][1].x, fb[s][j][1].y};
         acc[i][j] = mfma32(H{}, b, a, acc[i][j]);
@@ -263,27 +282,36 @@ struct W8Gemm {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     grp = wave >> 2;
     gw = wave & 3;
-    const int wm = wave >> 2, wn = wave & 3;
-    A = static_cast<const uint16_t *>(p.A);
-    B = static_cast<const uint16_t *>(p.B);
-    if (grp == 0) ld.init<A_KC>(A, p.lda, m0, p.M, gw, lane, 0);
-    else ld.init<B_KC>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
+    if (TL::KSPLIT == 1) {   // groups split the rows: 128 x 64 blocks
+      wm = int(grp);
+      wn = int(gw);
+      ks0 = 0;
+    } else {                 // groups split K: 64 x 64 blocks, steps 2 grp, 2 grp + 1
+      wm = int(gw >> 1);
+      wn = int(gw & 1);
+      ks0 = 2 * grp;
+    }
+    const uint16_t *A = static_cast<const uint16_t *>(p.A), *B = static_cast<const uint16_t *>(p.B);
+    if (grp == 0) ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
+    else ld.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
+    // The wave's first step within a slab: K-contiguous reads move 32 bytes a step
+    // (chunk 2 s), M/N-contiguous ones 16 k-rows a step.
     if (A_KC) {
-      fa_off[0] = kc_lane(lane) + 2048 * 4 * wm;     // row blocks 4 wm .. 4 wm + 3
+      fa_off[0] = (kc_lane<BK>(lane) ^ (32 * ks0)) + 64 * BK * FM * wm;
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa_off[i] = mn_lane(lane, 4 * wm + i);
+      for (int i = 0; i < FM; ++i) fa_off[i] = mn_lane<BM>(lane, FM * wm + i) + 16 * ks0 * 2 * BM;
     }
     if (B_KC) {
-      fb_off[0] = kc_lane(lane) + 2048 * 2 * wn;     // column blocks 2 wn, 2 wn + 1
+      fb_off[0] = (kc_lane<BK>(lane) ^ (32 * ks0)) + 64 * BK * FN * wn;
     } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb_off[j] = mn_lane(lane, 2 * wn + j);
+      for (int j = 0; j < FN; ++j) fb_off[j] = mn_lane<BN>(lane, FN * wn + j) + 16 * ks0 * 2 * BN;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
     kdim = int(p.K);
     const int KT = (kdim + BK - 1) / BK;
 
@@ -314,30 +342,65 @@ struct W8Gemm {
       MHG_ORDER();
     }
     if (grp == 0) barrier();
-    // Loads past K (zeros) are still writing LDS: drain them before the workgroup ends.
+    // Loads past K (zeros) are still writing LDS: drain them, then let every wave
+    // finish with the ring before the epilogue reuses its memory.
     wait_vm<0>();
+    barrier();
     MHG_ORDER();
 
-    // acc[i][j] holds the transposed 32 x 32 block: element r of lane l is
-    // C[row 128 wm + 32 i + l % 32][col 64 wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of
-    // the tile.  A lane's four consecutive columns are a 16-byte piece of one row, and a
-    // store instruction would touch 32 rows; staged through LDS instead, every store
-    // writes whole 128-byte (16-bit C) or 256-byte (fp32 C) row segments.
+    if (TL::KSPLIT == 2) {
+      // Group 1 hands its partial sums to its partner wave of group 0 (same block of C)
+      // through LDS, lane-major so that neither side has bank conflicts.
+      const uint32_t handoff = lds0 + gw * (FM * FN * 16 * 64 * 4);
+      if (grp == 1) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              *reinterpret_cast<MHG_LDS f32x4 *>(size_t(handoff + (((i * FN + j) * 4 + q) * 64 + lane) * 16)) = v;
+            }
+      }
+      barrier();
+      if (grp == 1) return;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v = *reinterpret_cast<const MHG_LDS f32x4 *>(
+                size_t(handoff + (((i * FN + j) * 4 + q) * 64 + lane) * 16));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
+          }
+    }
+    // Staging areas: past the hand-off areas (4 x 16 KiB) when the groups split K.
+    epilogue(lane, TL::KSPLIT == 2 ? lds0 + 65536 + gw * 16384 : lds0 + wave * 16384);
+  }
+
+  // acc[i][j] holds the transposed 32 x 32 block: element r of lane l is
+  // C[row WTM wm + 32 i + l % 32][col WTN wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of
+  // the tile.  A lane's four consecutive columns are a 16-byte piece of one row, and a
+  // store instruction would touch 32 rows; staged through the wave's 16 KiB of LDS at
+  // `region` instead, every store writes whole 64-column row segments of C.
+  __device__ __forceinline__ void epilogue(int lane, uint32_t region) {
+    static_assert(FN == 2 && FM % 2 == 0, "staging assumes 64-column blocks of 64 or 128 rows");
     const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
     const int ob = p.out_code == E_F32 ? 4 : 2;
     const bool c16 = ((uintptr_t(p.C) | uintptr_t(p.ldc * ob)) & 15) == 0;
     if (c16) {
-      barrier();                        // every wave is done with the ring
-      const uint32_t region = lds0 + wave * 16384;
       if (p.out_code == E_F32) {
+        // 64 rows of 256 bytes a pass; chunk c of row r at 16 (c ^ (r % 16)): sixteen
+        // rows written at one chunk hit 16 bank groups
 #pragma unroll
-        for (int pass = 0; pass < 2; ++pass) {
-          // rows 64 pass .. +63 of the wave's block, 256 bytes a row; chunk c of row r
-          // at 16 (c ^ (r % 16)): sixteen rows written at one chunk hit 16 bank groups
+        for (int pass = 0; pass < FM / 2; ++pass) {
 #pragma unroll
           for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < FN; ++j)
 #pragma unroll
               for (int q = 0; q < 4; ++q) {
                 const int i = 2 * pass + i2, r = 32 * i2 + (lane & 31), c = 8 * j + 2 * q + (lane >> 5);
@@ -354,9 +417,9 @@ struct W8Gemm {
       } else {
         // 128 bytes a row; chunk c of row r at 16 (c ^ ((r / 2) % 8))
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
+          for (int j = 0; j < FN; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const int r = 32 * i + (lane & 31), c = 4 * j + q;
@@ -369,7 +432,7 @@ struct W8Gemm {
               *reinterpret_cast<MHG_LDS u32x2 *>(size_t(region + r * 128 + 16 * (c ^ ((r >> 1) & 7)) + 8 * (lane >> 5))) = v;
             }
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
+        for (int k = 0; k < WTM / 8; ++k) {
           const int r = 8 * k + (lane >> 3), c = lane & 7;
           const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 128 + 16 * (c ^ ((r >> 1) & 7))));
           store_chunk(rowW + r, colW + 8 * c, v, 8);
@@ -381,11 +444,11 @@ struct W8Gemm {
     const int64_t colL = colW + 4 * (lane >> 5);
     const bool c_vec = p.c_vec != 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < FM; ++i) {
       const int64_t row = row0 + 32 * i;
       if (row >= p.M) continue;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int64_t col = colL + 32 * j + 8 * q;
@@ -417,38 +480,48 @@ struct W8Gemm {
   }
 };
 
-template <class H, bool A_KC, bool B_KC>
+template <class H, bool A_KC, bool B_KC, class TL>
 __global__ void __launch_bounds__(NT)
 w8_gemm(LaunchArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES];
-  W8Gemm<H, A_KC, B_KC> g(p);
+  W8Gemm<H, A_KC, B_KC, TL> g(p);
   g.run(uint32_t(size_t((MHG_LDS char *)smem)));
 }
 
-#define MHG_W8_INST(H)                                            \
-  template __global__ void w8_gemm<H, true, false>(LaunchArgs);  \
-  template __global__ void w8_gemm<H, true, true>(LaunchArgs);   \
-  template __global__ void w8_gemm<H, false, false>(LaunchArgs); \
-  template __global__ void w8_gemm<H, false, true>(LaunchArgs);
-MHG_W8_INST(HalfBF16)
-MHG_W8_INST(HalfF16)
+#define MHG_W8_INST(H, TL)                                            \
+  template __global__ void w8_gemm<H, true, false, TL>(LaunchArgs);  \
+  template __global__ void w8_gemm<H, true, true, TL>(LaunchArgs);   \
+  template __global__ void w8_gemm<H, false, false, TL>(LaunchArgs); \
+  template __global__ void w8_gemm<H, false, true, TL>(LaunchArgs);
+MHG_W8_INST(HalfBF16, Tile256)
+MHG_W8_INST(HalfF16, Tile256)
+MHG_W8_INST(HalfBF16, Tile128)
+MHG_W8_INST(HalfF16, Tile128)
 #undef MHG_W8_INST
 
-template <class H>
+template <class H, class TL>
 hipError_t launch_typed(const LaunchArgs &p, hipStream_t s) {
   const dim3 grid(unsigned(p.gm) * unsigned(p.gn)), block(NT);
-  if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false>), grid, block, 0, s, p);
-  else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true>), grid, block, 0, s, p);
-  else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((w8_gemm<H, false, true>), grid, block, 0, s, p);
+  if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL>), grid, block, 0, s, p);
+  else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL>), grid, block, 0, s, p);
+  else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL>), grid, block, 0, s, p);
+  else hipLaunchKernelGGL((w8_gemm<H, false, true, TL>), grid, block, 0, s, p);
   return hipGetLastError();
+}
+
+template <class TL>
+hipError_t launch_tile(const LaunchArgs &p, hipStream_t s) {
+  if (p.in_code == E_BF16) return launch_typed<HalfBF16, TL>(p, s);
+  if (p.in_code == E_F16) return launch_typed<HalfF16, TL>(p, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace w8
 
-hipError_t launch_w8(const LaunchArgs &p, hipStream_t s) {
-  if (p.in_code == E_BF16) return w8::launch_typed<HalfBF16>(p, s);
-  if (p.in_code == E_F16) return w8::launch_typed<HalfF16>(p, s);
+// bm: 256 (256 x 256 tiles, 32-deep slabs) or 128 (128 x 128 tiles, 64-deep slabs).
+hipError_t launch_w8(const LaunchArgs &p, int bm, hipStream_t s) {
+  if (bm == 256) return w8::launch_tile<w8::Tile256>(p, s);
+  if (bm == 128) return w8::launch_tile<w8::Tile128>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -26,6 +26,7 @@ enum LauncherId {
   L_BIG_256,
   L_SKINNY,
   L_W8_256,
+  L_W8_128,
   L_COUNT
 };
 

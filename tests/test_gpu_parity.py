@@ -34,7 +34,7 @@ def _catalogue_for(in_t):
         return [(1, 32, 32, 32, 4, 1, 2, 1), (1, 64, 64, 16, 4, 1, 2, 1), (1, 128, 128, 16, 4, 1, 2, 1)]
     return [(2, 64, 64, 64, 2, 2, 2, 1), (2, 128, 128, 64, 2, 2, 2, 1), (2, 256, 128, 64, 2, 2, 2, 1),
             (2, 256, 256, 64, 2, 4, 2, 1), (2, 128, 128, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 2, 4, 1),
-            (2, 256, 256, 32, 2, 4, 4, 1), (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1)]
+            (2, 256, 256, 32, 2, 4, 4, 1), (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1)]
 
 
 # ---- the measured workloads at full size ---------------------------------------------------
@@ -114,7 +114,7 @@ def test_ragged_extents(in_t, out_t):
 
 
 ALIGNED_ONLY = {(2, 128, 128, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 4, 4, 1),
-                (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1)}
+                (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1)}
 ROW_MAJOR_A_ONLY = {(2, 256, 256, 64, 2, 2, 2, 1)}
 
 
@@ -173,34 +173,53 @@ def test_four_wave_256_kernel_every_slab_count(in_t, out_t, b_col):
 
 
 W8_256 = (2, 256, 256, 32, 2, 4, 5, 1)
+W8_128 = (2, 128, 128, 64, 2, 4, 5, 1)
 
 
-@pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
+@pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32"), ("f16", "f16")])
 @pytest.mark.parametrize("a_col,b_col", LAYOUTS)
-def test_eight_wave_256_kernel_every_slab_count(in_t, out_t, a_col, b_col):
-    """The 256 x 256 eight-wave kernel keeps a ring of five 32-deep slabs with three in
-    flight; K from one partial slab to more than two trips round the ring, on a ragged
-    grid, in every layout (K-contiguous operands read 16 bytes a lane, M/N-contiguous
-    ones through LDS transpose reads)."""
+@pytest.mark.parametrize("cfg", [W8_256, W8_128], ids=["256", "128"])
+def test_eight_wave_kernels_every_slab_count(in_t, out_t, a_col, b_col, cfg):
+    """The eight-wave kernels keep a ring of five slabs (32 deep at 256 x 256, 64 deep at
+    128 x 128) with four requested ahead; K from one partial slab to more than two trips
+    round the ring, on a ragged grid, in every layout (K-contiguous operands read 16
+    bytes a lane, M/N-contiguous ones through LDS transpose reads)."""
     M, N = 264, 520
-    for K in (8, 32, 40, 96, 160, 168, 328):
+    bk = cfg[3]
+    for K in (8, bk, bk + 8, 3 * bk, 5 * bk, 5 * bk + 8, 10 * bk + 8):
         As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, seed=K)
-        C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, cfg=W8_256)
-        assert (desc["bm"], desc["bn"], desc["threads"]) == (256, 256, 512)
+        C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, cfg=cfg)
+        assert (desc["bm"], desc["bn"], desc["threads"]) == (cfg[1], cfg[2], 512)
         Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
         check_tolerance(C, Cref, out_t, f"K={K} a_col={a_col} b_col={b_col}")
 
 
 @pytest.mark.parametrize("a_col,b_col", LAYOUTS)
-def test_eight_wave_256_kernel_exact_integer_sums(a_col, b_col):
-    """Dense integers in [-3, 3] over two full tiles in each direction: every fp32
-    partial sum is exact, so the bf16 output must be the oracle's rounding bit for bit
-    (a misplaced fragment, slab or wave block changes the sums)."""
+@pytest.mark.parametrize("cfg", [W8_256, W8_128], ids=["256", "128"])
+@pytest.mark.parametrize("out_t", ["f32", "bf16"])
+def test_eight_wave_kernels_exact_integer_sums(a_col, b_col, cfg, out_t):
+    """Dense integers in [-3, 3] over two full tiles in each direction (four at 128):
+    every fp32 partial sum is exact, so the output must be the oracle's rounding bit
+    for bit (for bf16 output: the oracle's round-to-nearest-even of the exact sum); a
+    misplaced fragment, slab, wave block, K half or staged store changes it."""
     M, N, K = 512, 512, 512
     As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "bf16", a_col, b_col, dist="int", r=3, seed=21)
-    C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "bf16", "f32", a_col, b_col, cfg=W8_256)
+    C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "bf16", out_t, a_col, b_col, cfg=cfg)
     Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16", a_col, b_col)
-    check_exact(raw, Cref, "f32", f"a_col={a_col} b_col={b_col}")
+    check_exact(raw, Cref, out_t, f"a_col={a_col} b_col={b_col}")
+
+
+@pytest.mark.parametrize("cfg", [W8_256, W8_128], ids=["256", "128"])
+@pytest.mark.parametrize("out_t", ["f32", "bf16"])
+def test_eight_wave_kernels_unaligned_c(cfg, out_t):
+    """C whose base or leading dimension is not 16-byte aligned takes the direct stores
+    instead of the LDS-staged ones; guard bands check both paths write nothing else."""
+    M, N, K = 264, 520, 136
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "bf16", seed=12)
+    Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16")
+    for offset_c, ldc in ((0, N), (1, N), (0, N + 4)):
+        C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "bf16", out_t, ldc=ldc, cfg=cfg, offset_c=offset_c)
+        check_tolerance(C, Cref, out_t, f"offset_c={offset_c} ldc={ldc}")
 
 
 def SKINNY(split):
