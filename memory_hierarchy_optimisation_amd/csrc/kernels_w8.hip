@@ -3,9 +3,10 @@
 // ring of K slabs.  Two tile shapes:
 //   * 256 x 256, 32-deep slabs: the two wave groups split the tile's rows, each wave
 //     owns 128 x 64 of C (4 x 2 accumulators of 32 x 32);
-//   * 128 x 128, 64-deep slabs: the two wave groups split each slab's K (first and
-//     second 32), each wave owns 64 x 64 of C (2 x 2 accumulators), and the two
-//     partial sums of a block are added through LDS at the end.
+//   * 128 x 128, 64-deep slabs: the two wave groups take alternate slabs (group 0 the
+//     even ones, group 1 the odd ones), each wave owns 64 x 64 of C (2 x 2
+//     accumulators), and the two partial sums of a block are added through LDS at the
+//     end.
 // Both slabs are 32 KiB (16 KiB of A at +0, 16 KiB of B at +16 KiB), so both shapes
 // use the same ring: five slots, 160 KB.
 //
@@ -23,7 +24,9 @@
 // Ping-pong: the waves form two groups, one wave of each per SIMD.  Block barriers
 // cut time into phases; in each phase one group runs the matrix instructions of a
 // slab back to back, with no memory instruction among them, while the other group
-// reads its fragments of the next slab from LDS and issues one operand's loads.  A
+// reads its fragments of the next slab from LDS and issues loads (at 256 x 256 each
+// group loads one operand of every slab; at 128 x 128 both operands of its own slabs).
+// Either way a phase holds 16 matrix instructions per wave.  A
 // wave that interleaves its own loads with its matrix instructions stalls at them, and
 // a SIMD whose two waves do the same thing at the same time stalls with them; here the
 // matrix pipe of every SIMD is fed by one wave while the other waits on memory.
@@ -56,7 +59,7 @@ constexpr int AHEAD = 4;                        // slab t+4 is requested while s
 constexpr uint32_t kOut = 0x80000000u;          // beyond every buffer range: loads zeros
 
 // The two tile shapes.  FM x FN accumulators of 32 x 32 per wave; KSPLIT = 2: the
-// groups take the first and second half of each slab's K instead of halves of the rows.
+// groups take alternate slabs (halves of K) instead of halves of the rows.
 struct Tile256 { static constexpr int BM = 256, BN = 256, BK = 32, FM = 4, FN = 2, KSPLIT = 1; };
 struct Tile128 { static constexpr int BM = 128, BN = 128, BK = 64, FM = 2, FN = 2, KSPLIT = 2; };
 
@@ -80,8 +83,8 @@ __device__ __forceinline__ uint32_t kc_off(int r, int c) { return uint32_t(r * 2
 template <int R>
 __device__ __forceinline__ uint32_t mn_off(int k, int c) { return uint32_t(k * 2 * R + 16 * (c ^ (4 * (k & 3)))); }
 
-// The slab loads of one wave.  Each group loads one operand: group 0 A, group 1 B.
-// The four waves of a group fill an operand's 16 KiB slab: load j of group wave w
+// The slab loads of one wave for one operand.  The four waves of a group fill an
+// operand's 16 KiB slab: load j of group wave w
 // fills LDS bytes (4 j + w) * 1024 .. +1023 of it; lane l writes chunk slot
 // (4 j + w) * 64 + l and loads the chunk that belongs there.
 struct Loader {
@@ -177,6 +180,8 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 template <class H, bool A_KC, bool B_KC, class TL>
 struct W8Gemm {
   static constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, FM = TL::FM, FN = TL::FN;
+  static constexpr bool ALT = TL::KSPLIT == 2;           // groups take alternate slabs
+  static constexpr int STEPS = BK / 16;                  // 16-deep steps of a slab
   static constexpr int WTM = 32 * FM, WTN = 32 * FN;      // a wave's block of C
   static_assert(BM * BK * 2 == OP_BYTES && BN * BK * 2 == OP_BYTES, "slab size");
 
@@ -186,16 +191,17 @@ struct W8Gemm {
   uint32_t lds0;
   uint32_t grp, gw;           // group (0: waves 0-3, 1: waves 4-7), wave within the group
   int wm, wn;                 // the wave's block of C: rows WTM wm, columns WTN wn
-  uint32_t ks0;               // first 16-deep step of each slab the wave multiplies
-  Loader ld;                  // group 0 loads A, group 1 loads B
-  // Lane offsets of the fragment reads within an operand slab (for the wave's first
-  // step), the wave's block offset included: K-contiguous operands use [0] (the second
-  // step is [0] ^ 32, block i adds 64 BK i); M/N-contiguous ones one per block.
+  // 256 x 256: ld is the group's operand (group 0 A, group 1 B); 128 x 128: ld is A and
+  // ld2 B of the group's own slabs.
+  Loader ld, ld2;
+  // Lane offsets of the fragment reads within an operand slab (step 0), the wave's
+  // block offset included: K-contiguous operands use [0] (step s is [0] ^ 32 s, block i
+  // adds 64 BK i); M/N-contiguous ones one per block (step s adds 16 s k-rows).
   uint32_t fa_off[FM], fb_off[FN];
   f32x16 acc[FM][FN];
   // The fragments of one slab, [step][block][half] (k 0..3 and 4..7 of the lane's
   // eight): a 16-byte read fills both halves, a transpose read one.
-  u32x2 fa[2][FM][2], fb[2][FN][2];
+  u32x2 fa[STEPS][FM][2], fb[STEPS][FN][2];
 
   static constexpr int NA = A_KC ? 1 : 2, NB = B_KC ? 1 : 2;
   static constexpr int T = FN * NB + FM * NA;            // LDS reads per step
@@ -230,36 +236,49 @@ struct W8Gemm {
       }
     }
   }
-  // Reads K .. T-1 of step S; the group's two loads of the step go after reads 1 and
-  // T / 2 + 1 (T >= 6, so both exist).
+  // Reads K .. T-1 of step S, with two loads of slab t + 4 after reads 1 and T / 2 + 1
+  // (T >= 6, so both exist): at 256 x 256 loads 2 S and 2 S + 1 of the group's operand,
+  // at 128 x 128 load S of A and load S of B.
   template <int S, int K>
   __device__ __forceinline__ void reads_from(uint32_t slot, int t) {
     if constexpr (K < T) {
       read<S, K>(slot); MHG_ORDER();
-      if constexpr (K == 1 || K == T / 2 + 1) { issue(t + AHEAD, 2 * S + (K != 1)); MHG_ORDER(); }
+      if constexpr (K == 1 || K == T / 2 + 1) {
+        const int k0 = (t + AHEAD) * BK;
+        const uint32_t dst = slot_addr(t + AHEAD);
+        if constexpr (ALT) (K == 1 ? ld : ld2).issue(k0, kdim - k0, dst, gw, S);
+        else ld.issue(k0, kdim - k0, dst, gw, 2 * S + (K != 1));
+        MHG_ORDER();
+      }
       reads_from<S, K + 1>(slot, t);
     }
   }
-  // Load j (of 4) of slab t for this wave's group: A for group 0, B for group 1.
-  __device__ __forceinline__ void issue(int t, int j) const {
+  // Every load of slab t this wave makes (prologue).
+  __device__ __forceinline__ void issue_all(int t) const {
     const int k0 = t * BK;
-    ld.issue(k0, kdim - k0, slot_addr(t), gw, j);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      ld.issue(k0, kdim - k0, slot_addr(t), gw, j);
+      if (ALT) ld2.issue(k0, kdim - k0, slot_addr(t), gw, j);
+    }
   }
 
   // Memory phase for slab t: read all of the wave's fragments of slab t and request
-  // its group's operand of slab t+4 (into the slot of slab t-1, which both groups have
-  // finished reading: the last reader ended its phase with every read complete).
+  // loads of slab t+4 (into the slot of slab t-1, which every wave has finished
+  // reading: the last reader ended its phase with every read complete).
+  template <int S>
+  __device__ __forceinline__ void mem_steps(uint32_t slot, int t) {
+    if constexpr (S < STEPS) { reads_from<S, 0>(slot, t); mem_steps<S + 1>(slot, t); }
+  }
   __device__ __forceinline__ void mem(int t) {
-    const uint32_t slot = slot_addr(t);
-    reads_from<0, 0>(slot, t);
-    reads_from<1, 0>(slot, t);
+    mem_steps<0>(slot_addr(t), t);
     wait_lgkm<0>();
     MHG_ORDER();
   }
-  // Compute phase: the wave's 2 FM FN matrix instructions of a slab, back to back.
+  // Compute phase: the wave's STEPS FM FN matrix instructions of a slab, back to back.
   __device__ __forceinline__ void compute() {
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < STEPS; ++s)
 #pragma unroll
       for (int m = 0; m < FM * FN; ++m) {
         const int i = m / FN, j = m % FN;
@@ -282,31 +301,29 @@ struct W8Gemm {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     grp = wave >> 2;
     gw = wave & 3;
-    if (TL::KSPLIT == 1) {   // groups split the rows: 128 x 64 blocks
+    const uint16_t *A = static_cast<const uint16_t *>(p.A), *B = static_cast<const uint16_t *>(p.B);
+    if (!ALT) {              // groups split the rows (128 x 64 blocks) and the operands
       wm = int(grp);
       wn = int(gw);
-      ks0 = 0;
-    } else {                 // groups split K: 64 x 64 blocks, steps 2 grp, 2 grp + 1
+      if (grp == 0) ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
+      else ld.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
+    } else {                 // groups take alternate slabs; 64 x 64 blocks
       wm = int(gw >> 1);
       wn = int(gw & 1);
-      ks0 = 2 * grp;
+      ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
+      ld2.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
     }
-    const uint16_t *A = static_cast<const uint16_t *>(p.A), *B = static_cast<const uint16_t *>(p.B);
-    if (grp == 0) ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
-    else ld.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
-    // The wave's first step within a slab: K-contiguous reads move 32 bytes a step
-    // (chunk 2 s), M/N-contiguous ones 16 k-rows a step.
     if (A_KC) {
-      fa_off[0] = (kc_lane<BK>(lane) ^ (32 * ks0)) + 64 * BK * FM * wm;
+      fa_off[0] = kc_lane<BK>(lane) + 64 * BK * FM * wm;
     } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa_off[i] = mn_lane<BM>(lane, FM * wm + i) + 16 * ks0 * 2 * BM;
+      for (int i = 0; i < FM; ++i) fa_off[i] = mn_lane<BM>(lane, FM * wm + i);
     }
     if (B_KC) {
-      fb_off[0] = (kc_lane<BK>(lane) ^ (32 * ks0)) + 64 * BK * FN * wn;
+      fb_off[0] = kc_lane<BK>(lane) + 64 * BK * FN * wn;
     } else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb_off[j] = mn_lane<BN>(lane, FN * wn + j) + 16 * ks0 * 2 * BN;
+      for (int j = 0; j < FN; ++j) fb_off[j] = mn_lane<BN>(lane, FN * wn + j);
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -317,29 +334,53 @@ struct W8Gemm {
 
     // Every wave runs the same loop, mem(t); barrier; compute(); barrier, but group 1
     // passes one extra barrier before it and group 0 one after it, so group 1 runs one
-    // phase behind: in phase 2t group 0 reads slab t while group 1 multiplies slab t-1,
-    // in phase 2t+1 group 0 multiplies slab t while group 1 reads it.  Group 0 requests
-    // A of slab t+4 in phase 2t, group 1 B of slab t+4 in phase 2t+1; slab t+1 must be
-    // in LDS when phase 2t+2 starts, so before every barrier each wave waits until at
-    // most its three younger slabs' loads (12) are in flight.
+    // phase behind and the two groups of a SIMD alternate between reading and
+    // multiplying.
     wait_lgkm<0>();                     // nothing else counts against lgkmcnt below
+    if (!ALT) {
+      // Both groups read every slab: in phase 2t group 0 reads slab t while group 1
+      // multiplies slab t-1, in phase 2t+1 group 0 multiplies slab t while group 1 reads
+      // it.  Group 0 requests A of slab t+4 in phase 2t, group 1 B of slab t+4 in phase
+      // 2t+1; slab t+1 must be in LDS when phase 2t+2 starts, so before every barrier
+      // each wave waits until at most its three younger slabs' loads (12) are in flight.
 #pragma unroll
-    for (int t = 0; t < AHEAD; ++t)
-#pragma unroll
-      for (int j = 0; j < LOADS; ++j) issue(t, j);
-    wait_vm<3 * LOADS>();               // slab 0 landed
-    barrier();
-    if (grp == 1) barrier();
-    MHG_ORDER();
-    for (int t = 0; t < KT; ++t) {
-      mem(t);
-      wait_vm<3 * LOADS>();
+      for (int t = 0; t < AHEAD; ++t) issue_all(t);
+      wait_vm<3 * LOADS>();             // slab 0 landed
       barrier();
+      if (grp == 1) barrier();
       MHG_ORDER();
-      compute();
-      wait_vm<3 * LOADS>();
+      for (int t = 0; t < KT; ++t) {
+        mem(t);
+        wait_vm<3 * LOADS>();
+        barrier();
+        MHG_ORDER();
+        compute();
+        wait_vm<3 * LOADS>();
+        barrier();
+        MHG_ORDER();
+      }
+    } else {
+      // Group g reads, requests and multiplies the slabs t = g mod 2: slab t is read in
+      // phase t and multiplied in phase t + 1, and slab t + 4 (the group's own) is
+      // requested while slab t is read.  Slab t + 2 must be in LDS when phase t + 2
+      // starts, so after multiplying a wave waits until only its slab t + 4 (8 loads) is
+      // in flight; slabs past K load zeros, so both groups run the same trip count.
+      issue_all(int(grp));
+      issue_all(int(grp) + 2);
+      wait_vm<2 * LOADS>();             // the group's first slab landed
       barrier();
+      if (grp == 1) barrier();
       MHG_ORDER();
+      for (int u = 0; u < (KT + 1) / 2; ++u) {
+        mem(2 * u + int(grp));
+        wait_vm<4 * LOADS>();
+        barrier();
+        MHG_ORDER();
+        compute();
+        wait_vm<2 * LOADS>();
+        barrier();
+        MHG_ORDER();
+      }
     }
     if (grp == 0) barrier();
     // Loads past K (zeros) are still writing LDS: drain them, then let every wave
