@@ -208,7 +208,7 @@ int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stre
         e = mhg::launch_ring(v->launcher, a, s); break;
       case mhg::L_BIG_256:
         e = mhg::launch_big(a, s); break;
-      case mhg::L_W8_256: case mhg::L_W8_128:
+      case mhg::L_W8_256: case mhg::L_W8_128: case mhg::L_W8_64:
         e = mhg::launch_w8(a, v->cfg.bm, s); break;
       case mhg::L_SKINNY:
         e = mhg::launch_skinny(a, s); break;

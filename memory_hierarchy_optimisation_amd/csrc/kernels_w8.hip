@@ -1,20 +1,23 @@
 // kernels_w8.hip -- fp16 / bf16 GEMM for large aligned problems: eight waves (two per
 // SIMD) in a ping-pong schedule, both operands loaded straight into a five-slot LDS
-// ring of K slabs.  Two tile shapes:
+// ring of K slabs.  Three tile shapes:
 //   * 256 x 256, 32-deep slabs: the two wave groups split the tile's rows, each wave
 //     owns 128 x 64 of C (4 x 2 accumulators of 32 x 32);
 //   * 128 x 128, 64-deep slabs: the two wave groups take alternate slabs (group 0 the
 //     even ones, group 1 the odd ones), each wave owns 64 x 64 of C (2 x 2
 //     accumulators), and the two partial sums of a block are added through LDS at the
-//     end.
-// Both slabs are 32 KiB (16 KiB of A at +0, 16 KiB of B at +16 KiB), so both shapes
-// use the same ring: five slots, 160 KB.
+//     end;
+//   * 64 x 64, 128-deep slabs: as 128 x 128, with 32 x 32 of C per wave.
+// Every slab is 32 KiB (16 KiB of A at +0, 16 KiB of B at +16 KiB), so all shapes use
+// the same ring: five slots, 160 KB, four slabs requested ahead.
 //
 // The three tiling levels of "Tiling 策略与内存层次优化" (multi-level tiling) sized for
 // gfx950:
 //   * workgroup tile: 256 x 256 has tile intensity 2*256*256 / (512*2) = 128 FLOP/B
 //     (same page, how tiling raises intensity) and covers 4096^2 with one tile per
-//     compute unit; 128 x 128 (64 FLOP/B) covers 2048^2 the same way;
+//     compute unit; 128 x 128 (64 FLOP/B) covers 2048^2 the same way and 64 x 64
+//     (32 FLOP/B) covers 1024^2, where the product is short and load latency, not
+//     reuse, decides: four 128-deep slabs in flight are half of K;
 //   * K slabs in a ring of five 32 KiB LDS slots (constraint 1 of the same page with
 //     stages = 5), requested four slabs ahead with 16-byte LDS-destination buffer
 //     loads, the gfx950 counterpart of cp.async (cp.async section);
@@ -58,10 +61,11 @@ constexpr int LOADS = OP_BYTES / (GROUP * 64 * 16);   // 16-byte loads per lane 
 constexpr int AHEAD = 4;                        // slab t+4 is requested while slab t is read
 constexpr uint32_t kOut = 0x80000000u;          // beyond every buffer range: loads zeros
 
-// The two tile shapes.  FM x FN accumulators of 32 x 32 per wave; KSPLIT = 2: the
-// groups take alternate slabs (halves of K) instead of halves of the rows.
+// The tile shapes.  FM x FN accumulators of 32 x 32 per wave; KSPLIT = 2: the groups
+// take alternate slabs (halves of K) instead of halves of the rows.
 struct Tile256 { static constexpr int BM = 256, BN = 256, BK = 32, FM = 4, FN = 2, KSPLIT = 1; };
 struct Tile128 { static constexpr int BM = 128, BN = 128, BK = 64, FM = 2, FN = 2, KSPLIT = 2; };
+struct Tile64 { static constexpr int BM = 64, BN = 64, BK = 128, FM = 1, FN = 1, KSPLIT = 2; };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
@@ -71,17 +75,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
 // of R rows (m or n) and slabs BK deep:
 //   K-contiguous: row r (0..R-1) of BK/8 16-byte k-chunks; chunk c at
 //     r * 2BK + 16 (c ^ kswz(r)), kswz(r) = (r >> 2) & 3 for 4 chunks a row,
-//     (r >> 1) & 7 for 8.  Sixteen consecutive rows read at one chunk (a fragment read,
-//     16 lanes an LDS cycle) land on 16 distinct 16-byte bank groups.
+//     (r >> 1) & 7 for 8, r & 15 for 16.  Sixteen consecutive rows read at one chunk (a
+//     fragment read, 16 lanes an LDS cycle) land on 16 distinct 16-byte bank groups.
 //   M/N-contiguous: k-row k (0..BK-1) of R/8 chunks of 8 m/n-values; chunk c at
-//     k * 2R + 16 (c ^ 4 (k & 3)).  A transpose read touches four consecutive k-rows,
-//     64 bytes each; the XOR moves them to four distinct quarters of the banks.
+//     k * 2R + 16 (c ^ mswz(k)).  A transpose read touches four consecutive k-rows, 64
+//     bytes each, in one LDS cycle; mswz(k) = 4 (k & 3) moves 512- or 256-byte k-rows
+//     to four distinct quarters of the banks, 4 ((k >> 1) & 1) the 128-byte k-rows of
+//     the 64-wide tile (rows k and k+1 already sit half the banks apart).
 template <int BK>
-__device__ __forceinline__ constexpr int kswz(int r) { return BK == 32 ? (r >> 2) & 3 : (r >> 1) & 7; }
+__device__ __forceinline__ constexpr int kswz(int r) {
+  return BK == 32 ? (r >> 2) & 3 : BK == 64 ? (r >> 1) & 7 : r & 15;
+}
+template <int R>
+__device__ __forceinline__ constexpr int mswz(int k) { return R >= 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
 template <int BK>
 __device__ __forceinline__ uint32_t kc_off(int r, int c) { return uint32_t(r * 2 * BK + 16 * (c ^ kswz<BK>(r))); }
 template <int R>
-__device__ __forceinline__ uint32_t mn_off(int k, int c) { return uint32_t(k * 2 * R + 16 * (c ^ (4 * (k & 3)))); }
+__device__ __forceinline__ uint32_t mn_off(int k, int c) { return uint32_t(k * 2 * R + 16 * (c ^ mswz<R>(k))); }
 
 // The slab loads of one wave for one operand.  The four waves of a group fill an
 // operand's 16 KiB slab: load j of group wave w
@@ -109,7 +119,7 @@ struct Loader {
         kin[j] = mn0 + r < MN ? 8 * c : 1 << 30;
       } else {
         constexpr int CPK = R / 8;                        // chunks a k-row
-        const int k = slot / CPK, c = (slot % CPK) ^ (4 * (k & 3));
+        const int k = slot / CPK, c = (slot % CPK) ^ mswz<R>(k);
         off[j] = uint32_t((int64_t(k) * ld + 8 * c) * 2);
         kin[j] = mn0 + 8 * c < MN ? k : 1 << 30;
       }
@@ -132,14 +142,16 @@ struct Loader {
 // v_mfma_f32_32x32x16: lane l holds row l % 32, k = 8 (l / 32) .. +7 of the 16-deep
 // step s.
 //   K-contiguous: one 16-byte read at kc_off(32 b + l % 32, 2 s + l / 32).  The swizzle
-//     term depends on the lane only (32 b leaves bits 0..4 of the row alone), and 2 s
-//     has no bit in common with l / 32 or with the swizzle's low bit, so step s is an
-//     XOR of 32 s on the lane's offset and block b a constant 32 b * 2BK.
+//     term depends on the lane only (32 b leaves bits 0..4 of the row alone), and
+//     (2 s + l / 32) ^ x = 2 s ^ (l / 32 ^ x) since 2 s has no bit in common with l / 32,
+//     so step s is an XOR of 32 s on the lane's offset (below the row's 2BK bytes) and
+//     block b a constant 32 b * 2BK.
 //   M/N-contiguous: two transpose reads (e = 0, 1) for k = 8 (l / 32) + 4 e .. +3.  In
 //     each 16-lane group g = l / 16, lane 4 q + u addresses the 8 bytes of k-row
 //     16 s + 8 (g / 2) + 4 e + q, columns 32 b + 16 (g % 2) + 4 u .. +3, and lane t then
 //     receives column 32 b + 16 (g % 2) + t of those four k-rows; step s adds 16 s * 2R
-//     and e adds 4 * 2R to the lane's offset for step 0, e = 0.
+//     and e adds 4 * 2R to the lane's offset for step 0, e = 0 (mswz depends on k's low
+//     two bits only, which are q's).
 template <int BK>
 __device__ __forceinline__ uint32_t kc_lane(int lane) { return kc_off<BK>(lane & 31, lane >> 5); }
 template <int R>
@@ -236,17 +248,19 @@ struct W8Gemm {
       }
     }
   }
-  // Reads K .. T-1 of step S, with two loads of slab t + 4 after reads 1 and T / 2 + 1
-  // (T >= 6, so both exist): at 256 x 256 loads 2 S and 2 S + 1 of the group's operand,
-  // at 128 x 128 load S of A and load S of B.
+  // Reads K .. T-1 of step S, interleaved with the loads of slab t + 4.  256 x 256:
+  // loads 2 S and 2 S + 1 of the group's operand after reads 1 and T / 2 + 1 (T >= 6,
+  // so both exist).  Groups on alternate slabs: load S of A after read 0 and load S of
+  // B after read 1, for the first LOADS steps (T >= 2).
   template <int S, int K>
   __device__ __forceinline__ void reads_from(uint32_t slot, int t) {
     if constexpr (K < T) {
       read<S, K>(slot); MHG_ORDER();
-      if constexpr (K == 1 || K == T / 2 + 1) {
+      constexpr bool load_here = ALT ? (S < LOADS && K < 2) : (K == 1 || K == T / 2 + 1);
+      if constexpr (load_here) {
         const int k0 = (t + AHEAD) * BK;
         const uint32_t dst = slot_addr(t + AHEAD);
-        if constexpr (ALT) (K == 1 ? ld : ld2).issue(k0, kdim - k0, dst, gw, S);
+        if constexpr (ALT) (K == 0 ? ld : ld2).issue(k0, kdim - k0, dst, gw, S);
         else ld.issue(k0, kdim - k0, dst, gw, 2 * S + (K != 1));
         MHG_ORDER();
       }
@@ -307,7 +321,7 @@ struct W8Gemm {
       wn = int(gw);
       if (grp == 0) ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
       else ld.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
-    } else {                 // groups take alternate slabs; 64 x 64 blocks
+    } else {                 // groups take alternate slabs; WTM x WTN blocks, 2 x 2 of them
       wm = int(gw >> 1);
       wn = int(gw & 1);
       ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
@@ -428,11 +442,13 @@ struct W8Gemm {
   // store instruction would touch 32 rows; staged through the wave's 16 KiB of LDS at
   // `region` instead, every store writes whole 64-column row segments of C.
   __device__ __forceinline__ void epilogue(int lane, uint32_t region) {
-    static_assert(FN == 2 && FM % 2 == 0, "staging assumes 64-column blocks of 64 or 128 rows");
     const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
     const int ob = p.out_code == E_F32 ? 4 : 2;
+    // Staging is laid out for 64-column blocks of 64 or 128 rows; the 32 x 32 blocks of
+    // the 64 x 64 tile (2 KiB of C a wave) store directly.
+    constexpr bool STAGE = FN == 2 && FM % 2 == 0;
     const bool c16 = ((uintptr_t(p.C) | uintptr_t(p.ldc * ob)) & 15) == 0;
-    if (c16) {
+    if (STAGE && c16) {
       if (p.out_code == E_F32) {
         // 64 rows of 256 bytes a pass; chunk c of row r at 16 (c ^ (r % 16)): sixteen
         // rows written at one chunk hit 16 bank groups
@@ -538,6 +554,8 @@ MHG_W8_INST(HalfBF16, Tile256)
 MHG_W8_INST(HalfF16, Tile256)
 MHG_W8_INST(HalfBF16, Tile128)
 MHG_W8_INST(HalfF16, Tile128)
+MHG_W8_INST(HalfBF16, Tile64)
+MHG_W8_INST(HalfF16, Tile64)
 #undef MHG_W8_INST
 
 template <class H, class TL>
@@ -559,10 +577,12 @@ hipError_t launch_tile(const LaunchArgs &p, hipStream_t s) {
 
 }  // namespace w8
 
-// bm: 256 (256 x 256 tiles, 32-deep slabs) or 128 (128 x 128 tiles, 64-deep slabs).
+// bm: 256 (256 x 256 tiles, 32-deep slabs), 128 (128 x 128 tiles, 64-deep slabs) or
+// 64 (64 x 64 tiles, 128-deep slabs).
 hipError_t launch_w8(const LaunchArgs &p, int bm, hipStream_t s) {
   if (bm == 256) return w8::launch_tile<w8::Tile256>(p, s);
   if (bm == 128) return w8::launch_tile<w8::Tile128>(p, s);
+  if (bm == 64) return w8::launch_tile<w8::Tile64>(p, s);
   return hipErrorInvalidValue;
 }
 

@@ -37,6 +37,7 @@ const Variant kCatalogue[] = {
     {{GEMM_KIND_FMA, 32, 32, 32, 4, 1, 2, 1}, 256, kF32, L_FMA_32, 2, 2, -1},
     {{GEMM_KIND_FMA, 64, 64, 16, 4, 1, 2, 1}, 256, kF32, L_FMA_64, 4, 4, -1},
     {{GEMM_KIND_FMA, 128, 128, 16, 4, 1, 2, 1}, 256, kF32, L_FMA_128, 8, 8, -1},
+    {{GEMM_KIND_MFMA, 64, 64, 128, 2, 4, 5, 1}, 512, kHalf, L_W8_64, 2, 2, L_MFMA_64x64},
     {{GEMM_KIND_MFMA, 64, 64, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_64x64, 2, 2, -1},
     {{GEMM_KIND_MFMA, 128, 128, 64, 2, 4, 5, 1}, 512, kHalf, L_W8_128, 4, 4, L_MFMA_128x128},
     {{GEMM_KIND_MFMA, 128, 128, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_128x128_W4, 4, 4, L_MFMA_128x128},
@@ -73,7 +74,7 @@ double best_intensity(int elem, unsigned mask) {
 // MFMA: 4 fp32 per 16x16 block + fragments + staged 16-byte chunks.
 int regs_estimate(const Variant &v) {
   if (v.launcher == L_BIG_256) return 512;   // one wave per SIMD: 256 accumulators in AGPRs
-  if (v.launcher == L_W8_256 || v.launcher == L_W8_128) return 256;   // two waves per SIMD
+  if (v.launcher == L_W8_256 || v.launcher == L_W8_128 || v.launcher == L_W8_64) return 256;   // two waves per SIMD
   if (v.launcher == L_SKINNY) return 128;    // 8 accumulators, two staged rounds, transposes
   if (is_ring(v.launcher)) {   // accumulators + two fragment sets + addressing
     return v.tm * v.tn * 4 + 2 * (v.tm + v.tn) * 4 + 24;
@@ -209,7 +210,8 @@ bool ring_shape_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bo
 }
 
 bool needs_aligned_staging(int launcher) {
-  return is_ring(launcher) || launcher == L_BIG_256 || launcher == L_W8_256 || launcher == L_W8_128;
+  return is_ring(launcher) || launcher == L_BIG_256 || launcher == L_W8_256 || launcher == L_W8_128 ||
+         launcher == L_W8_64;
 }
 
 bool skinny_shape_ok(const PlanData &p, std::string *why) {

@@ -27,6 +27,7 @@ enum LauncherId {
   L_SKINNY,
   L_W8_256,
   L_W8_128,
+  L_W8_64,
   L_COUNT
 };
 

@@ -34,7 +34,8 @@ def _catalogue_for(in_t):
         return [(1, 32, 32, 32, 4, 1, 2, 1), (1, 64, 64, 16, 4, 1, 2, 1), (1, 128, 128, 16, 4, 1, 2, 1)]
     return [(2, 64, 64, 64, 2, 2, 2, 1), (2, 128, 128, 64, 2, 2, 2, 1), (2, 256, 128, 64, 2, 2, 2, 1),
             (2, 256, 256, 64, 2, 4, 2, 1), (2, 128, 128, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 2, 4, 1),
-            (2, 256, 256, 32, 2, 4, 4, 1), (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1)]
+            (2, 256, 256, 32, 2, 4, 4, 1), (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1),
+            (2, 64, 64, 128, 2, 4, 5, 1)]
 
 
 # ---- the measured workloads at full size ---------------------------------------------------
@@ -114,7 +115,8 @@ def test_ragged_extents(in_t, out_t):
 
 
 ALIGNED_ONLY = {(2, 128, 128, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 4, 4, 1),
-                (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1)}
+                (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1),
+                (2, 64, 64, 128, 2, 4, 5, 1)}
 ROW_MAJOR_A_ONLY = {(2, 256, 256, 64, 2, 2, 2, 1)}
 
 
@@ -174,11 +176,12 @@ def test_four_wave_256_kernel_every_slab_count(in_t, out_t, b_col):
 
 W8_256 = (2, 256, 256, 32, 2, 4, 5, 1)
 W8_128 = (2, 128, 128, 64, 2, 4, 5, 1)
+W8_64 = (2, 64, 64, 128, 2, 4, 5, 1)
 
 
 @pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32"), ("f16", "f16")])
 @pytest.mark.parametrize("a_col,b_col", LAYOUTS)
-@pytest.mark.parametrize("cfg", [W8_256, W8_128], ids=["256", "128"])
+@pytest.mark.parametrize("cfg", [W8_256, W8_128, W8_64], ids=["256", "128", "64"])
 def test_eight_wave_kernels_every_slab_count(in_t, out_t, a_col, b_col, cfg):
     """The eight-wave kernels keep a ring of five slabs (32 deep at 256 x 256, 64 deep at
     128 x 128) with four requested ahead; K from one partial slab to more than two trips
@@ -195,10 +198,10 @@ def test_eight_wave_kernels_every_slab_count(in_t, out_t, a_col, b_col, cfg):
 
 
 @pytest.mark.parametrize("a_col,b_col", LAYOUTS)
-@pytest.mark.parametrize("cfg", [W8_256, W8_128], ids=["256", "128"])
+@pytest.mark.parametrize("cfg", [W8_256, W8_128, W8_64], ids=["256", "128", "64"])
 @pytest.mark.parametrize("out_t", ["f32", "bf16"])
 def test_eight_wave_kernels_exact_integer_sums(a_col, b_col, cfg, out_t):
-    """Dense integers in [-3, 3] over two full tiles in each direction (four at 128):
+    """Dense integers in [-3, 3] over two full tiles in each direction (four at 128, eight at 64):
     every fp32 partial sum is exact, so the output must be the oracle's rounding bit
     for bit (for bf16 output: the oracle's round-to-nearest-even of the exact sum); a
     misplaced fragment, slab, wave block, K half or staged store changes it."""
@@ -209,7 +212,7 @@ def test_eight_wave_kernels_exact_integer_sums(a_col, b_col, cfg, out_t):
     check_exact(raw, Cref, out_t, f"a_col={a_col} b_col={b_col}")
 
 
-@pytest.mark.parametrize("cfg", [W8_256, W8_128], ids=["256", "128"])
+@pytest.mark.parametrize("cfg", [W8_256, W8_128, W8_64], ids=["256", "128", "64"])
 @pytest.mark.parametrize("out_t", ["f32", "bf16"])
 def test_eight_wave_kernels_unaligned_c(cfg, out_t):
     """C whose base or leading dimension is not 16-byte aligned takes the direct stores
