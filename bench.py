@@ -201,7 +201,22 @@ def summarize_traffic(fetch_csv, write_csv, name, digest, out_path):
         f"traffic_bytes_per_launch: {traffic:.0f}",
         f"algorithmic_bytes_per_launch: {alg:.0f}",
         f"traffic_over_algorithmic: {traffic / alg:.3f}",
+        "# commands (run from /tmp with TMPDIR=/tmp), each its own run:",
+        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o f -- python3 bench.py --no-cpu-baseline "
+        "--no-per-shape --steps 20 --warmup 2 --copy-reference",
+        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o w -- python3 bench.py --no-cpu-baseline "
+        "--no-per-shape --steps 20 --warmup 2 --copy-reference",
+        "#   rocpd2csv -i gpurun_out/prof_fetch/f_results.db -d pmc_csv/fetch ; "
+        "rocpd2csv -i gpurun_out/prof_write/w_results.db -d pmc_csv/write",
+        f"#   python3 bench.py --workload {name} --summarize-traffic pmc_csv/fetch/out_counter_collection_trace.csv "
+        "pmc_csv/write/out_counter_collection_trace.csv <kernel_source_digest>",
+        "# The copy reference is torch's elementwise multiply over 512 MiB (reads and writes 524288 KiB):",
+        f"# FETCH_SIZE reads {fetch[c] / ref_kib:.2f} of the bytes read (scale {f_scale:.2f}), "
+        f"WRITE_SIZE {write[c] / ref_kib:.2f} of the bytes written (scale {w_scale:.2f}).",
     ]
+    if name == "bf16_4096":
+        lines += ["# Each XCD owns a 4 x 8 block of the 16 x 16 tiles, so every A panel is fetched by 2 XCDs and",
+                  "# every B panel by 4: 96 panels of 2 MiB = 192 MiB, the fetch above."]
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     log("\n".join(lines))
