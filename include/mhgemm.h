@@ -156,6 +156,54 @@ const char *gemm_last_error(void);
  */
 int gemm_plan_describe(gemm_plan_t plan, int32_t out[16]);
 
+/*
+ * gemm_catalogue -- the compiled variants, the candidate set of autotuning.
+ * Writes min(count, max_cfgs) configurations as 8 int32 each (the layout of
+ * gemm_plan_config's cfg) to cfgs (may be NULL) and returns the count.
+ */
+int gemm_catalogue(int32_t *cfgs, int32_t max_cfgs);
+
+/*
+ * gemm_autotune -- measure every compiled variant on one problem and keep the
+ * fastest ("Tiling 策略与内存层次优化", autotuning section: enumerate the tile
+ * configurations, filter out those that break the hardware limits, benchmark each
+ * on the target, choose the best).
+ *
+ * The problem arguments are those of gemm_plan; A, B and C are the caller's device
+ * operands in that layout (C is overwritten with the product).  Each variant that
+ * gemm_plan_config accepts for the problem runs twice untimed, then twice `reps`
+ * calls (1 <= reps <= 100000) between HIP events on `stream`; its time is the better
+ * batch's mean per call.  The fastest configuration is stored in a process-wide
+ * table that gemm_plan consults for this exact problem (all eight arguments equal)
+ * before its heuristic; a plan already made is not changed.  Outputs, each optional:
+ * best_cfg[8] (the gemm_plan_config layout), *best_us, and times_us[i] for catalogue
+ * entry i < n_times (microseconds per call, -1 for a variant that does not fit).
+ * Synchronises `stream`; allocates and frees split-K workspaces of the candidates.
+ * Returns GEMM_OK, GEMM_ERR_INVALID_ARG (bad problem, empty product, NULL operand,
+ * reps out of range, n_times > 0 with NULL times_us), GEMM_ERR_UNSUPPORTED (no variant
+ * fits) or GEMM_ERR_HIP (a candidate failed to run; message names it).  Thread-safe
+ * with respect to the table; do not run it concurrently on the same C.
+ */
+int gemm_autotune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                  int dtype, int layout, const void *A, const void *B, void *C, void *stream,
+                  int32_t reps, int32_t best_cfg[8], float *best_us, float *times_us, int32_t n_times);
+
+/*
+ * gemm_tune_save / gemm_tune_load / gemm_tune_clear -- the table of tuned choices.
+ * The file is text: '#' comment lines, then one line per problem,
+ *     M N K lda ldb ldc dtype layout | kind BM BN BK waves_m waves_n stages split_k | us
+ * save writes the whole table and returns the number of entries; load checks every
+ * line (a valid non-empty problem, a compiled configuration), then merges all of
+ * them into the table (an entry replaces one for the same problem) and returns
+ * their number; on any bad line it loads nothing and returns GEMM_ERR_INVALID_ARG
+ * with the line number in gemm_last_error.  A stored configuration that no longer
+ * fits when gemm_plan runs (for instance another compute-unit count) is ignored
+ * there in favour of the heuristic.  clear empties the table.
+ */
+int gemm_tune_save(const char *path);
+int gemm_tune_load(const char *path);
+void gemm_tune_clear(void);
+
 #ifdef __cplusplus
 }
 #endif

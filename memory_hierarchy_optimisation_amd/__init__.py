@@ -38,7 +38,8 @@ DESCRIBE_FIELDS = ("kind", "bm", "bn", "bk", "waves_m", "waves_n", "stages", "sp
                    "workspace_bytes")
 
 EXPORTS = ("gemm_plan", "gemm_plan_config", "gemm_run", "gemm_destroy", "gemm_last_error",
-           "gemm_plan_describe")
+           "gemm_plan_describe", "gemm_catalogue", "gemm_autotune", "gemm_tune_save",
+           "gemm_tune_load", "gemm_tune_clear")
 
 
 class GemmError(RuntimeError):
@@ -79,6 +80,18 @@ def _load():
     lib.gemm_last_error.restype = ctypes.c_char_p
     lib.gemm_plan_describe.argtypes = [vp, ctypes.POINTER(ctypes.c_int32)]
     lib.gemm_plan_describe.restype = i32
+    f32p, i32p = ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)
+    lib.gemm_catalogue.argtypes = [i32p, i32]
+    lib.gemm_catalogue.restype = i32
+    lib.gemm_autotune.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, i32,
+                                  i32p, f32p, f32p, i32]
+    lib.gemm_autotune.restype = i32
+    lib.gemm_tune_save.argtypes = [ctypes.c_char_p]
+    lib.gemm_tune_save.restype = i32
+    lib.gemm_tune_load.argtypes = [ctypes.c_char_p]
+    lib.gemm_tune_load.restype = i32
+    lib.gemm_tune_clear.argtypes = []
+    lib.gemm_tune_clear.restype = None
     runtimes = hip_runtimes_mapped()
     if len(runtimes) > 1:
         raise ImportError("more than one HIP runtime is mapped into this process "
@@ -148,3 +161,46 @@ def gemm_plan_describe(plan):
     if rc != GEMM_OK:
         raise GemmError(rc, gemm_last_error())
     return dict(zip(DESCRIBE_FIELDS, list(out)))
+
+
+def gemm_catalogue():
+    """Compiled variants as (kind, BM, BN, BK, waves_m, waves_n, stages, split_k) tuples."""
+    n = _lib.gemm_catalogue(None, 0)
+    arr = (ctypes.c_int32 * (8 * n))()
+    _lib.gemm_catalogue(arr, n)
+    return [tuple(arr[8 * i:8 * i + 8]) for i in range(n)]
+
+
+def gemm_autotune(M, N, K, lda, ldb, ldc, dtype, layout, A, B, C, stream=None, reps=20):
+    """Time every variant that fits on these operands and record the fastest for gemm_plan.
+    Returns (best configuration tuple, its microseconds per call, per-catalogue-entry
+    times with -1 for variants that do not fit).  Synchronises the stream."""
+    n = _lib.gemm_catalogue(None, 0)
+    best = (ctypes.c_int32 * 8)()
+    best_us = ctypes.c_float()
+    times = (ctypes.c_float * n)()
+    rc = _lib.gemm_autotune(M, N, K, lda, ldb, ldc, dtype, layout, _ptr(A), _ptr(B), _ptr(C),
+                            _stream(stream), int(reps), best, ctypes.byref(best_us), times, n)
+    if rc != GEMM_OK:
+        raise GemmError(rc, gemm_last_error())
+    return tuple(best), best_us.value, list(times)
+
+
+def gemm_tune_save(path):
+    """Write the table of tuned configurations; returns the number of entries."""
+    rc = _lib.gemm_tune_save(os.fsencode(path))
+    if rc < 0:
+        raise GemmError(rc, gemm_last_error())
+    return rc
+
+
+def gemm_tune_load(path):
+    """Merge a saved table of tuned configurations; returns the number of entries."""
+    rc = _lib.gemm_tune_load(os.fsencode(path))
+    if rc < 0:
+        raise GemmError(rc, gemm_last_error())
+    return rc
+
+
+def gemm_tune_clear():
+    _lib.gemm_tune_clear()

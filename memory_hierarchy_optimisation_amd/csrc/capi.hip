@@ -65,7 +65,24 @@ gemm_plan_t make_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
     return nullptr;
   }
   const mhg::Hardware hw = query_hardware();
-  const bool ok = cfg ? mhg::force(&d, hw, cfg, &err) : mhg::select(&d, hw, &err);
+  // A configuration measured fastest for exactly this problem (gemm_autotune, or a
+  // table read by gemm_tune_load) wins over the heuristic while it still fits.
+  bool ok;
+  if (cfg) {
+    ok = mhg::force(&d, hw, cfg, &err);
+  } else {
+    bool tuned_ok = false;
+    int32_t tuned[8];
+    if (M > 0 && N > 0 && K > 0 && mhg::tuned_lookup(M, N, K, lda, ldb, ldc, dtype, layout, tuned)) {
+      mhg::PlanData t = d;
+      std::string ignored;
+      if (mhg::force(&t, hw, tuned, &ignored)) {
+        d = t;
+        tuned_ok = true;
+      }
+    }
+    ok = tuned_ok || mhg::select(&d, hw, &err);
+  }
   if (!ok) {
     set_error(err);
     return nullptr;
@@ -126,6 +143,10 @@ int ensure_workspace(gemm_plan_s *plan, hipStream_t s) {
 }
 
 }  // namespace
+
+namespace mhg {
+void set_last_error(const std::string &msg) { set_error(msg); }
+}  // namespace mhg
 
 extern "C" {
 

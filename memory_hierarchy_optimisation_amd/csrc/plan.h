@@ -135,4 +135,9 @@ bool select(PlanData *p, const Hardware &hw, std::string *err);
 // Force a configuration; fails if it is not compiled or infeasible.
 bool force(PlanData *p, const Hardware &hw, const int32_t cfg[8], std::string *err);
 
+// Configuration recorded for exactly this problem by gemm_autotune or gemm_tune_load
+// (tune.cpp); false when there is none.
+bool tuned_lookup(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+                  int layout, int32_t cfg[8]);
+
 }  // namespace mhg

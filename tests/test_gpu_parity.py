@@ -28,14 +28,10 @@ LAYOUTS = list(itertools.product((False, True), repeat=2))
 
 
 def _catalogue_for(in_t):
-    """Every compiled configuration for an input type, found by forcing each entry of
-    a small list of known shapes (kept in sync with the planner's catalogue)."""
-    if in_t == "f32":
-        return [(1, 32, 32, 32, 4, 1, 2, 1), (1, 64, 64, 16, 4, 1, 2, 1), (1, 128, 128, 16, 4, 1, 2, 1)]
-    return [(2, 64, 64, 64, 2, 2, 2, 1), (2, 128, 128, 64, 2, 2, 2, 1), (2, 256, 128, 64, 2, 2, 2, 1),
-            (2, 256, 256, 64, 2, 4, 2, 1), (2, 128, 128, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 2, 4, 1),
-            (2, 256, 256, 32, 2, 4, 4, 1), (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1),
-            (2, 64, 64, 128, 2, 4, 5, 1)]
+    """Every compiled tile configuration for an input type (the library's catalogue,
+    without the M <= 16 split-K variants, which have tests of their own)."""
+    kind = mh.GEMM_KIND_FMA if in_t == "f32" else mh.GEMM_KIND_MFMA
+    return [c for c in mh.gemm_catalogue() if c[0] == kind]
 
 
 # ---- the measured workloads at full size ---------------------------------------------------
