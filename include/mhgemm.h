@@ -140,6 +140,38 @@ gemm_plan_t gemm_plan_config(int64_t M, int64_t N, int64_t K, int64_t lda, int64
  */
 int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stream);
 
+/* Activation of the fused epilogue. */
+enum gemm_activation {
+    GEMM_ACT_NONE = 0,
+    GEMM_ACT_RELU = 1    /* max(t, 0); anything not above zero, NaN included, becomes +0 */
+};
+
+/* Fused epilogue: element-wise work on the product tile on its way to C. */
+typedef struct gemm_epilogue {
+    float alpha;         /* multiplies the accumulated product */
+    float beta;          /* multiplies the prior contents of C; 0: C is only written */
+    const float *bias;   /* device pointer to N fp32 values added to every row, or NULL */
+    int32_t activation;  /* gemm_activation, applied last */
+} gemm_epilogue_t;
+
+/*
+ * gemm_run_epilogue -- gemm_run with a fused epilogue ("Tiling 策略与内存层次优化",
+ * fusion stage: element-wise post-processing such as bias add or ReLU done on the
+ * GEMM tile's output before it is written back to HBM):
+ *
+ *     C[i][j] = act(alpha * sum_k A(i,k) B(k,j) + beta * C_prior[i][j] + bias[j])
+ *
+ * evaluated in fp32 (C_prior converted exactly from the output type), then rounded
+ * once to the output type as in gemm_run.  beta == 0 reads nothing from C; bias may
+ * be NULL; K == 0 gives act(beta * C_prior + bias).  epi == NULL, or alpha 1, beta 0,
+ * no bias and no activation, is exactly gemm_run.  Same operands, stream semantics
+ * and status codes as gemm_run; GEMM_ERR_INVALID_ARG also for an unknown activation
+ * or a bias pointer that is not 4-byte aligned.  With beta != 0, C must hold valid
+ * values of the output type, and C must not alias the bias.
+ */
+int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C,
+                      const gemm_epilogue_t *epi, void *stream);
+
 /* gemm_destroy -- release a plan and its workspace.  NULL is ignored. */
 void gemm_destroy(gemm_plan_t plan);
 

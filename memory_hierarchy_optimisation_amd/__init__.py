@@ -22,6 +22,7 @@ GEMM_F32_F32, GEMM_F16_F16, GEMM_F16_F32, GEMM_BF16_BF16, GEMM_BF16_F32 = range(
 GEMM_A_ROW, GEMM_A_COL, GEMM_B_ROW, GEMM_B_COL = 0, 1, 0, 2
 GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED, GEMM_ERR_HIP, GEMM_ERR_ALLOC = 0, -1, -2, -3, -4
 GEMM_KIND_NONE, GEMM_KIND_FMA, GEMM_KIND_MFMA, GEMM_KIND_SKINNY = range(4)
+GEMM_ACT_NONE, GEMM_ACT_RELU = 0, 1
 
 # (input element, output element) of each gemm_dtype, and back.
 DTYPES = {
@@ -37,9 +38,15 @@ DESCRIBE_FIELDS = ("kind", "bm", "bn", "bk", "waves_m", "waves_n", "stages", "sp
                    "grid_x", "grid_y", "grid_z", "threads", "lds_bytes", "cus", "variant",
                    "workspace_bytes")
 
-EXPORTS = ("gemm_plan", "gemm_plan_config", "gemm_run", "gemm_destroy", "gemm_last_error",
-           "gemm_plan_describe", "gemm_catalogue", "gemm_autotune", "gemm_tune_save",
+EXPORTS = ("gemm_plan", "gemm_plan_config", "gemm_run", "gemm_run_epilogue", "gemm_destroy",
+           "gemm_last_error", "gemm_plan_describe", "gemm_catalogue", "gemm_autotune", "gemm_tune_save",
            "gemm_tune_load", "gemm_tune_clear")
+
+
+class Epilogue(ctypes.Structure):
+    """gemm_epilogue_t: C = act(alpha * product + beta * prior C + bias[column])."""
+    _fields_ = [("alpha", ctypes.c_float), ("beta", ctypes.c_float), ("bias", ctypes.c_void_p),
+                ("activation", ctypes.c_int32)]
 
 
 class GemmError(RuntimeError):
@@ -74,6 +81,8 @@ def _load():
     lib.gemm_plan_config.restype = vp
     lib.gemm_run.argtypes = [vp, vp, vp, vp, vp]
     lib.gemm_run.restype = i32
+    lib.gemm_run_epilogue.argtypes = [vp, vp, vp, vp, ctypes.POINTER(Epilogue), vp]
+    lib.gemm_run_epilogue.restype = i32
     lib.gemm_destroy.argtypes = [vp]
     lib.gemm_destroy.restype = None
     lib.gemm_last_error.argtypes = []
@@ -147,6 +156,16 @@ def _stream(stream):
 def gemm_run(plan, A, B, C, stream=None):
     """Enqueue the planned product on ``stream`` (default: torch's current stream)."""
     rc = _lib.gemm_run(plan, _ptr(A), _ptr(B), _ptr(C), _stream(stream))
+    if rc != GEMM_OK:
+        raise GemmError(rc, gemm_last_error())
+
+
+def gemm_run_epilogue(plan, A, B, C, alpha=1.0, beta=0.0, bias=None, activation=GEMM_ACT_NONE,
+                      stream=None):
+    """Enqueue C = act(alpha * A x B + beta * C + bias[column]) (bias: N fp32 values on
+    the device, or None) on ``stream``."""
+    epi = Epilogue(float(alpha), float(beta), _ptr(bias), int(activation))
+    rc = _lib.gemm_run_epilogue(plan, _ptr(A), _ptr(B), _ptr(C), ctypes.byref(epi), _stream(stream))
     if rc != GEMM_OK:
         raise GemmError(rc, gemm_last_error())
 

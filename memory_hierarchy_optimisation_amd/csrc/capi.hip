@@ -165,8 +165,21 @@ gemm_plan_t gemm_plan_config(int64_t M, int64_t N, int64_t K, int64_t lda, int64
 }
 
 int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stream) {
+  return gemm_run_epilogue(plan, A, B, C, nullptr, stream);
+}
+
+int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, const gemm_epilogue_t *epi,
+                      void *stream) {
   if (!plan) {
     set_error("gemm_run: NULL plan");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (epi && epi->activation != GEMM_ACT_NONE && epi->activation != GEMM_ACT_RELU) {
+    set_error("gemm_run_epilogue: unknown activation");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (epi && epi->bias && reinterpret_cast<uintptr_t>(epi->bias) % 4 != 0) {
+    set_error("gemm_run_epilogue: bias must be 4-byte aligned fp32");
     return GEMM_ERR_INVALID_ARG;
   }
   const mhg::PlanData &d = plan->d;
@@ -189,6 +202,18 @@ int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stre
   a.gn = d.gn;
   a.split_k = d.gz;
   a.group_m = d.group_m;
+  // The identity epilogue is the plain product: the kernels then skip it entirely.
+  a.alpha = 1.0f;
+  a.beta = 0.0f;
+  a.bias = nullptr;
+  a.act = GEMM_ACT_NONE;
+  if (epi) {
+    a.alpha = epi->alpha;
+    a.beta = epi->beta;
+    a.bias = epi->bias;
+    a.act = epi->activation;
+    a.epi = !(a.alpha == 1.0f && a.beta == 0.0f && !a.bias && a.act == GEMM_ACT_NONE);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d.K == 0) {

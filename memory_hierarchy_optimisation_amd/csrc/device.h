@@ -119,4 +119,33 @@ __device__ __forceinline__ void store_out(void *C, int64_t idx, float v, int out
   }
 }
 
+// Output element -> fp32 (exact: every fp16 / bf16 value is an fp32 value).
+__device__ __forceinline__ float load_out(const void *C, int64_t idx, int out_code) {
+  if (out_code == E_F32) return reinterpret_cast<const float *>(C)[idx];
+  if (out_code == E_F16) return float(reinterpret_cast<const _Float16 *>(C)[idx]);
+  return float(reinterpret_cast<const __bf16 *>(C)[idx]);
+}
+
+// The fused epilogue on one accumulated element of C[row][col], in fp32, before the
+// single rounding to the output type: element-wise work done on the tile's output on
+// its way to HBM ("Tiling 策略与内存层次优化", fusion stage: bias and ReLU fused into
+// the GEMM tile's output end).  beta == 0 reads nothing from C, so C's prior contents
+// (even NaN) do not matter then.  ReLU maps everything that is not above zero (NaN
+// included) to +0.
+__device__ __forceinline__ float epilogue1(const LaunchArgs &p, float v, int64_t row, int64_t col) {
+  float t = p.alpha * v;
+  if (p.beta != 0.0f) t += p.beta * load_out(p.C, row * p.ldc + col, p.out_code);
+  if (p.bias) t += p.bias[col];
+  if (p.act == 1) t = t > 0.0f ? t : 0.0f;
+  return t;
+}
+
+// The same on C[row][col .. col + 3]; elements e >= n_in (past N) are left as they are.
+__device__ __forceinline__ f32x4 epilogue4(const LaunchArgs &p, f32x4 v, int64_t row, int64_t col, int64_t n_in) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    if (e < n_in) v[e] = epilogue1(p, v[e], row, col + e);
+  return v;
+}
+
 }  // namespace mhg

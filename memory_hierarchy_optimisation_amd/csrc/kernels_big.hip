@@ -435,7 +435,8 @@ struct BigGemm {
           const int64_t col = colL + 32 * j + 8 * q;
           const int64_t n_in = p.N - col;
           if (n_in <= 0) continue;
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (p.epi) v = epilogue4(p, v, row, col, n_in);
           store_out4(p.C, row * p.ldc + col, v, p.out_code, c_vec && n_in >= 4, int(n_in));
         }
     }

@@ -109,7 +109,8 @@ fma_gemm(LaunchArgs p) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
       const int64_t col = n0 + tx * TN + j;
-      if (row < p.M && col < p.N) store_out(p.C, row * p.ldc + col, acc[i][j], p.out_code);
+      if (row < p.M && col < p.N)
+        store_out(p.C, row * p.ldc + col, p.epi ? epilogue1(p, acc[i][j], row, col) : acc[i][j], p.out_code);
     }
   }
 }
@@ -129,12 +130,14 @@ hipError_t launch_fma_tiles(const LaunchArgs &p, hipStream_t s) {
 }
 
 // C = 0 for K = 0 (the empty sum), any output type.
-__global__ void fill_zero(void *C, int64_t M, int64_t N, int64_t ldc, int out_code) {
-  const int64_t total = M * N;
+// K = 0: every element is the empty sum, 0, passed through the epilogue when there
+// is one (then C = act(beta * C + bias)).
+__global__ void fill_zero(LaunchArgs p) {
+  const int64_t total = p.M * p.N;
   for (int64_t e = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; e < total;
        e += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t i = e / N, j = e % N;
-    store_out(C, i * ldc + j, 0.f, out_code);
+    const int64_t i = e / p.N, j = e % p.N;
+    store_out(p.C, i * p.ldc + j, p.epi ? epilogue1(p, 0.f, i, j) : 0.f, p.out_code);
   }
 }
 
@@ -152,8 +155,7 @@ hipError_t launch_fma(int launcher, const LaunchArgs &p, hipStream_t s) {
 hipError_t launch_fill(const LaunchArgs &p, hipStream_t s) {
   const int64_t total = p.M * p.N;
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 4096);
-  hipLaunchKernelGGL(fill_zero, dim3(unsigned(std::max<int64_t>(blocks, 1))), dim3(256), 0, s, p.C,
-                     p.M, p.N, p.ldc, p.out_code);
+  hipLaunchKernelGGL(fill_zero, dim3(unsigned(std::max<int64_t>(blocks, 1))), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

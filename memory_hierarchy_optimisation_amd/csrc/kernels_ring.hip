@@ -214,7 +214,8 @@ ring_gemm(LaunchArgs p) {
       const int64_t col = n0 + wn * WTN + j * 16 + 4 * (lane >> 4);
       const int64_t n_in = p.N - col;
       if (n_in <= 0) continue;
-      store_out4(p.C, row * p.ldc + col, acc[i][j], p.out_code, p.c_vec && n_in >= 4, int(n_in));
+      const f32x4 v = p.epi ? epilogue4(p, acc[i][j], row, col, n_in) : acc[i][j];
+      store_out4(p.C, row * p.ldc + col, v, p.out_code, p.c_vec && n_in >= 4, int(n_in));
     }
   }
 }

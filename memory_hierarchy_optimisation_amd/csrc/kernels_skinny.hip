@@ -107,7 +107,8 @@ struct Skinny {
   __device__ void run(float (*red)[16][BN], int *last) {
     const int gn = p.gn, split = p.split_k;
     const int tn = int(blockIdx.x % unsigned(gn)), z = int(blockIdx.x / unsigned(gn));
-    const int wave = threadIdx.x >> 6;
+    // Uniform per wave: keeps the buffer resources of A and B in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
     lane = threadIdx.x & 63;
     g = lane >> 4;
     q = lane & 15;
@@ -166,6 +167,10 @@ struct Skinny {
       if (row >= p.M) return;
       const int64_t n_in = p.N - cg;
       if (n_in <= 0) return;
+      if (p.epi) {
+        a = epilogue4(p, a, row, cg, n_in);
+        b = epilogue4(p, b, row, cg + 4, n_in - 4);
+      }
       store_out4(p.C, row * p.ldc + cg, a, p.out_code, c_vec && n_in >= 4, int(n_in));
       if (n_in > 4) store_out4(p.C, row * p.ldc + cg + 4, b, p.out_code, c_vec && n_in >= 8, int(n_in - 4));
     };

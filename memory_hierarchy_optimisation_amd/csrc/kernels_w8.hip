@@ -93,6 +93,15 @@ __device__ __forceinline__ uint32_t kc_off(int r, int c) { return uint32_t(r * 2
 template <int R>
 __device__ __forceinline__ uint32_t mn_off(int k, int c) { return uint32_t(k * 2 * R + 16 * (c ^ mswz<R>(k))); }
 
+// A 64-bit value as the first lane holds it.  The builtin reads 32 bits and returns a
+// signed int: each half goes back to unsigned before it is widened, or a low half with
+// bit 31 set would sign-extend over the high half.
+__device__ __forceinline__ uint64_t first_lane_u64(uint64_t v) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v))));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readfirstlane(int(uint32_t(v >> 32))));
+  return (uint64_t(hi) << 32) | uint64_t(lo);
+}
+
 // The slab loads of one wave for one operand.  The four waves of a group fill an
 // operand's 16 KiB slab: load j of group wave w
 // fills LDS bytes (4 j + w) * 1024 .. +1023 of it; lane l writes chunk slot
@@ -124,8 +133,12 @@ struct Loader {
         kin[j] = mn0 + 8 * c < MN ? k : 1 << 30;
       }
     }
-    origin0 = KC ? g + int64_t(mn0) * ld : g + mn0;
-    kstep = KC ? 1 : ld;
+    // Both are the same on every lane; reading them through the first lane tells the
+    // compiler so, which keeps the buffer resource built from them in scalar registers
+    // (a resource it takes for per-lane wraps every load in a loop over lanes).
+    origin0 = reinterpret_cast<const uint16_t *>(
+        first_lane_u64(reinterpret_cast<uint64_t>(KC ? g + int64_t(mn0) * ld : g + mn0)));
+    kstep = int64_t(first_lane_u64(uint64_t(KC ? int64_t(1) : ld)));
     lds_off = area;
   }
   // Load j of the slab at k0 into `slot` (wave-uniform; so is `wave`, the wave's index
@@ -449,7 +462,9 @@ struct W8Gemm {
     constexpr bool STAGE = FN == 2 && FM % 2 == 0;
     const bool c16 = ((uintptr_t(p.C) | uintptr_t(p.ldc * ob)) & 15) == 0;
     if (STAGE && c16) {
-      if (p.out_code == E_F32) {
+      // With a fused epilogue every output type is staged as fp32, so that the epilogue
+      // (and beta's read of the prior C) works on whole row segments too.
+      if (p.out_code == E_F32 || p.epi) {
         // 64 rows of 256 bytes a pass; chunk c of row r at 16 (c ^ (r % 16)): sixteen
         // rows written at one chunk hit 16 bank groups
 #pragma unroll
@@ -468,7 +483,14 @@ struct W8Gemm {
           for (int k = 0; k < 16; ++k) {
             const int r = 4 * k + (lane >> 4), c = lane & 15;
             const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15))));
-            store_chunk(rowW + 64 * pass + r, colW + 4 * c, v, 4);
+            if (!p.epi) {
+              store_chunk(rowW + 64 * pass + r, colW + 4 * c, v, 4);
+              continue;
+            }
+            const int64_t row = rowW + 64 * pass + r, col = colW + 4 * c, n_in = p.N - col;
+            if (row >= p.M || n_in <= 0) continue;
+            const f32x4 f = epilogue4(p, __builtin_bit_cast(f32x4, v), row, col, n_in);
+            store_out4(p.C, row * p.ldc + col, f, p.out_code, n_in >= 4, int(n_in));
           }
         }
       } else {
@@ -511,7 +533,8 @@ struct W8Gemm {
           const int64_t col = colL + 32 * j + 8 * q;
           const int64_t n_in = p.N - col;
           if (n_in <= 0) continue;
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (p.epi) v = epilogue4(p, v, row, col, n_in);
           store_out4(p.C, row * p.ldc + col, v, p.out_code, c_vec && n_in >= 4, int(n_in));
         }
     }

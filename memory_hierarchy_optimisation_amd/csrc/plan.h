@@ -92,6 +92,12 @@ struct LaunchArgs {
   int group_m;        // rows of tiles walked together (L2 locality)
   void *workspace;
   int64_t ws_bytes;
+  // Fused epilogue, C = act(alpha * product + beta * prior C + bias[column]); epi = 0 is
+  // the plain product (alpha 1, beta 0, no bias, no activation) and skips all of it.
+  int epi;
+  float alpha, beta;
+  const float *bias;   // N fp32 values or NULL
+  int act;             // gemm_activation
 };
 
 struct PlanData {

@@ -142,3 +142,29 @@ def decode(bits, dtype):
 
 def max_threads():
     return int(_load().oracle_max_threads())
+
+
+def epilogue(S, alpha=1.0, beta=0.0, C_prior=None, bias=None, activation="none"):
+    """The fused epilogue on an exact product S (binary64, M x N): element-wise work on
+    the GEMM tile's output before it is written back ("Tiling 策略与内存层次优化",
+    fusion stage: bias add and ReLU fused into the tile's output end), with the usual
+    scaling of the product and of the prior C:
+
+        T[i][j] = act(alpha * S[i][j] + beta * C_prior[i][j] + bias[j]),
+
+    act = ReLU (everything not above zero, NaN included, becomes +0) or the identity.
+    alpha and beta are taken as the fp32 values a caller passes; C_prior is the
+    decoded prior C (binary64, exact), bias N fp32 values.  beta == 0 ignores C_prior.
+    Computed in binary64: T is exact whenever its terms are small integers."""
+    S = np.asarray(S, dtype=np.float64)
+    T = np.float64(np.float32(alpha)) * S
+    if np.float32(beta) != 0:
+        T = T + np.float64(np.float32(beta)) * np.asarray(C_prior, dtype=np.float64)
+    if bias is not None:
+        T = T + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
+    if activation == "relu":
+        T = np.where(T > 0, T, 0.0)
+    elif activation != "none":
+        raise ValueError(f"unknown activation {activation}")
+    return T
+

@@ -154,3 +154,16 @@ def from_storage_numpy(x, dtype):
         return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
     t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint16).view(np.int16))
     return t.view(TORCH_DTYPES[dtype])
+
+
+def epilogue_inputs(M, N, out_t, ldc=None, dist="uniform", seed=1, r=4):
+    """Prior C (M x ldc storage of the output type, padding columns NaN) and an fp32
+    bias of N values for the fused-epilogue tests, from one seeded generator (C first).
+    dist "uniform": both uniform on [-1, 1); "int": integers in [-r, r]."""
+    gen = torch.Generator().manual_seed(seed)
+    ldc = N if ldc is None else ldc
+    C = _draw(gen, (M, N), dist, out_t, r=r)
+    bias = _draw(gen, (N,), dist, "f32", r=r)
+    Cs, _ = lay_out(C, False, ldc)
+    return Cs, bias
+

@@ -35,9 +35,12 @@ def _to_device(storage, offset):
 
 
 def run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col=False, b_col=False, ldc=None, cfg=None,
-            offset_a=0, offset_b=0, offset_c=0):
+            offset_a=0, offset_b=0, offset_c=0, c_init=None, epi=None):
     """Run C = A x B on the GPU.  Returns (C values float64 [M,N], C raw storage [M,N]
-    numpy (uint16 patterns or float32), plan description)."""
+    numpy (uint16 patterns or float32), plan description).  ``c_init``: M x N (or wider)
+    CPU tensor of the output type written into C first (its first N columns; the rest of
+    C keeps the sentinel); ``epi``: keyword arguments of gemm_run_epilogue (alpha, beta,
+    bias as a CPU fp32 tensor, activation), else plain gemm_run."""
     ldc = N if ldc is None else ldc
     layout = (mh.GEMM_A_COL if a_col else 0) | (mh.GEMM_B_COL if b_col else 0)
     code = dtype_code(in_t, out_t)
@@ -50,13 +53,24 @@ def run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col=False, b_col=False, ld
     else:
         cbuf = torch.full((total,), SENTINEL16, dtype=torch.int16, device="cuda")
     C = cbuf[GUARD + offset_c:]
+    if c_init is not None and M and N:
+        view = C[:n_c].view(synth.TORCH_DTYPES[out_t]).view(M, ldc)
+        view[:, :N].copy_(c_init[:, :N].to("cuda"))
+    epi_dev = None
+    if epi is not None:
+        epi_dev = dict(epi)
+        if epi_dev.get("bias") is not None:
+            epi_dev["bias"] = epi_dev["bias"].to(torch.float32).cuda()
     if cfg is None:
         plan = mh.gemm_plan(M, N, K, lda, ldb, ldc, code, layout)
     else:
         plan = mh.gemm_plan_config(M, N, K, lda, ldb, ldc, code, layout, cfg)
     try:
         desc = mh.gemm_plan_describe(plan)
-        mh.gemm_run(plan, A, B, C)
+        if epi_dev is None:
+            mh.gemm_run(plan, A, B, C)
+        else:
+            mh.gemm_run_epilogue(plan, A, B, C, **epi_dev)
         torch.cuda.synchronize()
     finally:
         mh.gemm_destroy(plan)
