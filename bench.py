@@ -11,6 +11,10 @@ operand once (2MNK over the bytes of A, B and C).
 Operands rotate over enough copies that the working set exceeds the 256 MB
 Infinity Cache, so the bandwidth-bound shape streams from HBM.
 
+After the timed region: the headline shape once more through the fused epilogue
+(alpha = beta = 1, a bias, ReLU; "epilogue"), and for every shape but the 64^3 one an
+autotune sweep of the compiled variants against the planner's choice ("autotune").
+
 Prints ONE JSON line on stdout; everything else goes to stderr.
 """
 import argparse
@@ -63,8 +67,10 @@ def roofline_of(w):
     return ai, roof, bound
 
 
-def measure(name, steps, warmup, per_call=False):
-    """Time `steps` calls after `warmup` untimed calls.  Returns a dict of figures."""
+def measure(name, steps, warmup, per_call=False, epilogue=False):
+    """Time `steps` calls after `warmup` untimed calls.  Returns a dict of figures.
+    epilogue: run through the fused epilogue with alpha = beta = 1, a bias and ReLU
+    (C is read as well as written; its bytes and the bias's count in the GB/s)."""
     import torch
 
     import memory_hierarchy_optimisation_amd as mh
@@ -77,7 +83,7 @@ def measure(name, steps, warmup, per_call=False):
     A0, B0 = As.cuda(), Bs.cuda()
     As_dev = [A0] + [A0.clone() for _ in range(copies - 1)]
     Bs_dev = [B0] + [B0.clone() for _ in range(copies - 1)]
-    C = torch.empty((w.M, w.N), dtype=synth.TORCH_DTYPES[w.out], device="cuda")
+    C = torch.zeros((w.M, w.N), dtype=synth.TORCH_DTYPES[w.out], device="cuda")
     code = mh.DTYPE_OF[(w.dtype, w.out)]
     layout = (mh.GEMM_A_COL if w.a_col else 0) | (mh.GEMM_B_COL if w.b_col else 0)
     plan = mh.gemm_plan(w.M, w.N, w.K, lda, ldb, w.N, code, layout)
@@ -89,8 +95,14 @@ def measure(name, steps, warmup, per_call=False):
     b_ptr = [t.data_ptr() for t in Bs_dev]
     c_ptr, handle = C.data_ptr(), stream.cuda_stream
 
+    bias = torch.linspace(-1.0, 1.0, w.N, device="cuda") if epilogue else None
+
     def run(i):
-        mh.gemm_run(plan, a_ptr[i % copies], b_ptr[i % copies], c_ptr, handle)
+        if epilogue:
+            mh.gemm_run_epilogue(plan, a_ptr[i % copies], b_ptr[i % copies], c_ptr, alpha=1.0, beta=1.0,
+                                 bias=bias, activation=mh.GEMM_ACT_RELU, stream=handle)
+        else:
+            mh.gemm_run(plan, a_ptr[i % copies], b_ptr[i % copies], c_ptr, handle)
 
     try:
         for i in range(warmup):
@@ -118,10 +130,12 @@ def measure(name, steps, warmup, per_call=False):
     finally:
         mh.gemm_destroy(plan)
     flops, nbytes = algorithmic(w)
+    if epilogue:
+        nbytes += w.M * w.N * synth.ELEM_BYTES[w.out] + 4 * w.N
     ai, roof, bound = roofline_of(w)
     ms_step = wall * 1000.0 / steps
     out = {
-        "workload": name, "M": w.M, "N": w.N, "K": w.K, "in": w.dtype, "out": w.out,
+        "workload": name + ("+epilogue" if epilogue else ""), "M": w.M, "N": w.N, "K": w.K, "in": w.dtype, "out": w.out,
         "layout": ("A col" if w.a_col else "A row") + (", B col" if w.b_col else ", B row"),
         "tile": f"{desc['bm']}x{desc['bn']}x{desc['bk']}", "kind": desc["kind"],
         "grid": desc["grid_x"] * desc["grid_y"] * desc["grid_z"], "rotated_copies": copies,
@@ -135,6 +149,43 @@ def measure(name, steps, warmup, per_call=False):
     if calls:
         k = len(calls)
         out["kernel_ms_p10_p50_p90"] = [calls[k // 10], calls[k // 2], calls[(9 * k) // 10]]
+    return out
+
+
+def autotune_report(names, reps=10):
+    """For each workload: the planner's configuration, the fastest in an autotune sweep
+    of every compiled variant that fits (gemm_autotune), and their times.  The sweep's
+    table is cleared afterwards, so nothing timed elsewhere depends on it."""
+    import torch
+
+    import memory_hierarchy_optimisation_amd as mh
+    import synth
+
+    keys = ("kind", "bm", "bn", "bk", "waves_m", "waves_n", "stages", "split_k")
+    cat = mh.gemm_catalogue()
+    out = []
+    for name in names:
+        w = synth.WORKLOADS[name]
+        As, lda, Bs, ldb, _, _ = synth.workload_operands(w)
+        A, B = As.cuda(), Bs.cuda()
+        C = torch.empty((w.M, w.N), dtype=synth.TORCH_DTYPES[w.out], device="cuda")
+        code = mh.DTYPE_OF[(w.dtype, w.out)]
+        layout = (mh.GEMM_A_COL if w.a_col else 0) | (mh.GEMM_B_COL if w.b_col else 0)
+        plan = mh.gemm_plan(w.M, w.N, w.K, lda, ldb, w.N, code, layout)
+        d = mh.gemm_plan_describe(plan)
+        mh.gemm_destroy(plan)
+        heuristic = tuple(d[k] for k in keys)
+        try:
+            best, best_us, times = mh.gemm_autotune(w.M, w.N, w.K, lda, ldb, w.N, code, layout, A, B, C,
+                                                    reps=reps)
+        finally:
+            mh.gemm_tune_clear()
+        h_us = times[cat.index(heuristic)] if heuristic in cat else -1.0
+        out.append({"workload": name, "heuristic": list(heuristic), "heuristic_us": round(h_us, 3),
+                    "tuned": list(best), "tuned_us": round(best_us, 3),
+                    "candidates": sum(1 for t in times if t >= 0)})
+        log(f"[bench] autotune {name}: heuristic {heuristic} {h_us:.2f} us, fastest {best} {best_us:.2f} us "
+            f"of {out[-1]['candidates']} candidates")
     return out
 
 
@@ -266,6 +317,8 @@ def main():
     ap.add_argument("--workload", default=HEADLINE, help="workload timed as the headline")
     ap.add_argument("--no-per-shape", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the fused-epilogue line and the autotune sweep report")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-reference", action="store_true",
                     help="after timing, run one elementwise kernel of known traffic (counter scale)")
@@ -297,6 +350,13 @@ def main():
             shapes.append(r)
             log(f"[bench] {name}: {r['kernel_tflops']:.1f} TFLOP/s, {r['kernel_gbps']:.0f} GB/s, "
                 f"{100 * r['frac_of_roofline']:.1f}% of the {r['bound']} roofline, tile {r['tile']}")
+    extras = {}
+    if not args.no_per_shape and not args.no_extras:
+        r = measure(args.workload, 100, 20, per_call=True, epilogue=True)
+        extras["epilogue"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        log(f"[bench] {r['workload']} (alpha, beta = 1, bias, ReLU): {r['kernel_tflops']:.1f} TFLOP/s, "
+            f"kernel {r['kernel_ms_event'] * 1000:.1f} us against {head['kernel_ms_event'] * 1000:.1f} us plain")
+        extras["autotune"] = autotune_report([n for n in PER_SHAPE if n != "f32_64"])
     if args.copy_reference:
         copy_reference()
 
@@ -326,6 +386,7 @@ def main():
         "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                       for r in shapes],
     }
+    line.update(extras)
     print(json.dumps(line), flush=True)
 
 

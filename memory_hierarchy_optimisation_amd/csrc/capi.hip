@@ -211,6 +211,7 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
     a.alpha = epi->alpha;
     a.beta = epi->beta;
     a.bias = epi->bias;
+    a.bias_vec = reinterpret_cast<uintptr_t>(epi->bias) % 16 == 0;
     a.act = epi->activation;
     a.epi = !(a.alpha == 1.0f && a.beta == 0.0f && !a.bias && a.act == GEMM_ACT_NONE);
   }

@@ -140,12 +140,63 @@ __device__ __forceinline__ float epilogue1(const LaunchArgs &p, float v, int64_t
   return t;
 }
 
-// The same on C[row][col .. col + 3]; elements e >= n_in (past N) are left as they are.
-__device__ __forceinline__ f32x4 epilogue4(const LaunchArgs &p, f32x4 v, int64_t row, int64_t col, int64_t n_in) {
+// Prior C[row][col .. col + 3] as fp32 (elements past N read as 0): one 16- or 8-byte
+// load when all four lie inside the matrix and C allows vector access (col is a
+// multiple of 4 at every call site), else element by element.
+__device__ __forceinline__ f32x4 prior4(const LaunchArgs &p, int64_t row, int64_t col, int64_t n_in) {
+  const int64_t idx = row * p.ldc + col;
+  if (n_in >= 4 && p.c_vec) {
+    if (p.out_code == E_F32) return *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p.C) + idx);
+    const u32x2 h = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(p.C) + idx);
+    f32x4 c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t b = uint16_t(h[e >> 1] >> (16 * (e & 1)));
+      c[e] = p.out_code == E_F16 ? float(__builtin_bit_cast(_Float16, b)) : float(__builtin_bit_cast(__bf16, b));
+    }
+    return c;
+  }
+  f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if (e < n_in) v[e] = epilogue1(p, v[e], row, col + e);
+    if (e < n_in) c[e] = load_out(p.C, idx + e, p.out_code);
+  return c;
+}
+
+// bias[col .. col + 3] (0 past N or without a bias).
+__device__ __forceinline__ f32x4 bias4(const LaunchArgs &p, int64_t col, int64_t n_in) {
+  f32x4 b = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (p.bias) {
+    if (n_in >= 4 && p.bias_vec) {
+      b = *reinterpret_cast<const f32x4 *>(p.bias + col);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < n_in) b[e] = p.bias[col + e];
+    }
+  }
+  return b;
+}
+
+// The epilogue on C[row][col .. col + 3] given its prior values (ignored when beta is
+// 0) and its bias values; elements e >= n_in (past N) are left as they are.
+__device__ __forceinline__ f32x4 epilogue4pb(const LaunchArgs &p, f32x4 v, f32x4 prior, f32x4 b, int64_t n_in) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    if (e >= n_in) break;
+    float t = p.alpha * v[e];
+    if (p.beta != 0.0f) t += p.beta * prior[e];
+    t += b[e];
+    if (p.act == 1) t = t > 0.0f ? t : 0.0f;
+    v[e] = t;
+  }
   return v;
+}
+
+// The same, reading the prior and bias values itself.
+__device__ __forceinline__ f32x4 epilogue4(const LaunchArgs &p, f32x4 v, int64_t row, int64_t col, int64_t n_in) {
+  const f32x4 prior = p.beta != 0.0f ? prior4(p, row, col, n_in) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  return epilogue4pb(p, v, prior, bias4(p, col, n_in), n_in);
 }
 
 }  // namespace mhg

@@ -231,13 +231,21 @@ mfma_gemm(LaunchArgs p) {
   for (int i = 0; i < FM; ++i) {
     const int64_t row = m0 + wm * WTM + i * 16 + (lane & 15);
     if (row >= p.M) continue;
+    // With an epilogue, the row block's bias and prior values are requested before its
+    // first store (a load may not move above a store that might alias it).
+    if (p.epi) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int64_t col = n0 + wn * WTN + j * 16 + 4 * (lane >> 4);
+        if (col < p.N) acc[i][j] = epilogue4(p, acc[i][j], row, col, p.N - col);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int64_t col = n0 + wn * WTN + j * 16 + 4 * (lane >> 4);
       const int64_t n_in = p.N - col;
       if (n_in <= 0) continue;
-      const f32x4 v = p.epi ? epilogue4(p, acc[i][j], row, col, n_in) : acc[i][j];
-      store_out4(p.C, row * p.ldc + col, v, p.out_code, p.c_vec && n_in >= 4, int(n_in));
+      store_out4(p.C, row * p.ldc + col, acc[i][j], p.out_code, p.c_vec && n_in >= 4, int(n_in));
     }
   }
 }

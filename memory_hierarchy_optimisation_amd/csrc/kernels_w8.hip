@@ -462,9 +462,35 @@ struct W8Gemm {
     constexpr bool STAGE = FN == 2 && FM % 2 == 0;
     const bool c16 = ((uintptr_t(p.C) | uintptr_t(p.ldc * ob)) & 15) == 0;
     if (STAGE && c16) {
-      // With a fused epilogue every output type is staged as fp32, so that the epilogue
-      // (and beta's read of the prior C) works on whole row segments too.
-      if (p.out_code == E_F32 || p.epi) {
+      // A fused epilogue that reads the prior C (beta != 0), or that writes fp32, runs in
+      // the fp32 staging below, on whole row segments.  One that does not read C and
+      // writes a 16-bit type is applied to the accumulators here, before the 16-bit
+      // staging.  Either way the lane's bias chunks (and the pass's prior values of C)
+      // are requested before its first store: the compiler may not move a load above
+      // a store that might alias it.
+      if (p.epi && p.beta == 0.0f && p.out_code != E_F32) {
+        const int64_t colL = colW + 4 * (lane >> 5);
+        f32x4 b[FN][4];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = colL + 32 * j + 8 * q;
+            b[j][q] = col < p.N ? bias4(p, col, p.N - col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+              const f32x4 f = epilogue4pb(p, v, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, b[j][q], 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = f[e];
+            }
+      }
+      if (p.out_code == E_F32 || (p.epi && p.beta != 0.0f)) {
         // 64 rows of 256 bytes a pass; chunk c of row r at 16 (c ^ (r % 16)): sixteen
         // rows written at one chunk hit 16 bank groups
 #pragma unroll
@@ -479,18 +505,33 @@ struct W8Gemm {
                 const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
                 *reinterpret_cast<MHG_LDS f32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15)))) = v;
               }
+          if (!p.epi) {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+              const int r = 4 * k + (lane >> 4), c = lane & 15;
+              const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15))));
+              store_chunk(rowW + 64 * pass + r, colW + 4 * c, v, 4);
+            }
+            continue;
+          }
+          // A lane stores the same four columns in every row of the pass.
+          const int64_t colB = colW + 4 * (lane & 15);
+          const f32x4 bias = colB < p.N ? bias4(p, colB, p.N - colB) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          f32x4 prior[16];
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const int64_t row = rowW + 64 * pass + 4 * k + (lane >> 4);
+            prior[k] = p.beta != 0.0f && row < p.M && colB < p.N ? prior4(p, row, colB, p.N - colB)
+                                                                 : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          }
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
             const int r = 4 * k + (lane >> 4), c = lane & 15;
-            const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15))));
-            if (!p.epi) {
-              store_chunk(rowW + 64 * pass + r, colW + 4 * c, v, 4);
-              continue;
-            }
-            const int64_t row = rowW + 64 * pass + r, col = colW + 4 * c, n_in = p.N - col;
+            const int64_t row = rowW + 64 * pass + r, n_in = p.N - colB;
             if (row >= p.M || n_in <= 0) continue;
-            const f32x4 f = epilogue4(p, __builtin_bit_cast(f32x4, v), row, col, n_in);
-            store_out4(p.C, row * p.ldc + col, f, p.out_code, n_in >= 4, int(n_in));
+            const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15))));
+            const f32x4 f = epilogue4pb(p, __builtin_bit_cast(f32x4, v), prior[k], bias, n_in);
+            store_out4(p.C, row * p.ldc + colB, f, p.out_code, n_in >= 4, int(n_in));
           }
         }
       } else {
@@ -526,6 +567,19 @@ struct W8Gemm {
     for (int i = 0; i < FM; ++i) {
       const int64_t row = row0 + 32 * i;
       if (row >= p.M) continue;
+      // With an epilogue, the row block's bias and prior values are requested before its
+      // first store (a load may not move above a store that might alias it).
+      f32x4 ep[FN][4];
+      if (p.epi) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t col = colL + 32 * j + 8 * q;
+            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+            ep[j][q] = col < p.N ? epilogue4(p, v, row, col, p.N - col) : v;
+          }
+      }
 #pragma unroll
       for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -533,8 +587,8 @@ struct W8Gemm {
           const int64_t col = colL + 32 * j + 8 * q;
           const int64_t n_in = p.N - col;
           if (n_in <= 0) continue;
-          f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (p.epi) v = epilogue4(p, v, row, col, n_in);
+          const f32x4 v = p.epi ? ep[j][q]
+                                : f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
           store_out4(p.C, row * p.ldc + col, v, p.out_code, c_vec && n_in >= 4, int(n_in));
         }
     }

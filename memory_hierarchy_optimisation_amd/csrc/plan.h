@@ -97,6 +97,7 @@ struct LaunchArgs {
   int epi;
   float alpha, beta;
   const float *bias;   // N fp32 values or NULL
+  int bias_vec;        // 1: bias is 16-byte aligned (four values a load)
   int act;             // gemm_activation
 };
 
