@@ -13,7 +13,8 @@ Infinity Cache, so the bandwidth-bound shape streams from HBM.
 
 After the timed region: the headline shape once more through the fused epilogue
 (alpha = beta = 1, a bias, ReLU; "epilogue"), and for every shape but the 64^3 one an
-autotune sweep of the compiled variants against the planner's choice ("autotune").
+autotune sweep of the compiled variants against the planner's choice ("autotune"), and
+the tiled transpose of 8192^2 fp32 and 16-bit matrices ("transpose").
 
 Prints ONE JSON line on stdout; everything else goes to stderr.
 """
@@ -189,6 +190,42 @@ def autotune_report(names, reps=10):
     return out
 
 
+def transpose_report(shapes=((8192, 8192, 4), (8192, 8192, 2)), steps=50, warmup=10):
+    """The tiled transpose (gemm_transpose): GB/s counting each element read once and
+    written once, against the 8 TB/s HBM roofline; inputs rotate past the 256 MB cache."""
+    import torch
+
+    import memory_hierarchy_optimisation_amd as mh
+
+    out = []
+    for rows, cols, E in shapes:
+        dt = {2: torch.int16, 4: torch.int32}[E]
+        nbytes = rows * cols * E
+        # inputs and outputs both rotate: 2 x copies x nbytes > the 256 MB cache
+        copies = max(2, math.ceil(ROTATE_BYTES / (2 * nbytes)))
+        ins = [torch.zeros((rows, cols), dtype=dt, device="cuda") for _ in range(copies)]
+        outs = [torch.empty((cols, rows), dtype=dt, device="cuda") for _ in range(copies)]
+        ptrs = [t.data_ptr() for t in ins]
+        optrs = [t.data_ptr() for t in outs]
+        handle = torch.cuda.current_stream().cuda_stream
+        for i in range(warmup):
+            mh.gemm_transpose(ptrs[i % copies], optrs[(i + 1) % copies], rows, cols, cols, rows, E, stream=handle)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for i in range(steps):
+            mh.gemm_transpose(ptrs[i % copies], optrs[(i + 1) % copies], rows, cols, cols, rows, E, stream=handle)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / steps
+        gbps = 2 * nbytes / (ms / 1000.0) / 1e9
+        out.append({"rows": rows, "cols": cols, "elem_bytes": E, "kernel_ms_event": round(ms, 5),
+                    "gbps": round(gbps, 1), "frac_of_hbm": round(gbps / HBM_GBPS, 4)})
+        log(f"[bench] transpose {rows}x{cols} ({E}-byte elements): {ms * 1000:.1f} us, {gbps:.0f} GB/s, "
+            f"{100 * gbps / HBM_GBPS:.1f}% of HBM")
+        del ins, outs
+    return out
+
+
 def copy_reference(nbytes=512 << 20):
     """One elementwise device kernel of known traffic (reads and writes nbytes), run
     after the timed region so a counter run can scale FETCH_SIZE / WRITE_SIZE."""
@@ -357,6 +394,7 @@ def main():
         log(f"[bench] {r['workload']} (alpha, beta = 1, bias, ReLU): {r['kernel_tflops']:.1f} TFLOP/s, "
             f"kernel {r['kernel_ms_event'] * 1000:.1f} us against {head['kernel_ms_event'] * 1000:.1f} us plain")
         extras["autotune"] = autotune_report([n for n in PER_SHAPE if n != "f32_64"])
+        extras["transpose"] = transpose_report()
     if args.copy_reference:
         copy_reference()
 

@@ -172,6 +172,25 @@ typedef struct gemm_epilogue {
 int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C,
                       const gemm_epilogue_t *epi, void *stream);
 
+/*
+ * gemm_transpose -- out = transpose of in, the second tiled workload of "CUDA tile"
+ * (applications section: a tile staged through shared memory makes both the reads
+ * and the writes of a transpose coalesced):
+ *
+ *     out[c * ld_out + r] = in[r * ld_in + c],   0 <= r < rows, 0 <= c < cols.
+ *
+ * in: rows x cols, row-major, leading dimension ld_in >= cols; out: cols x rows,
+ * row-major, ld_out >= rows; both device pointers of elem_bytes-byte elements
+ * (2: fp16 / bf16, 4: fp32; the bytes are moved, not interpreted), aligned to the
+ * element.  Elements of out outside the cols x rows block are not touched; out must
+ * not overlap in.  Extents up to 2^31.  rows == 0 or cols == 0 is a no-op.
+ * Asynchronous on `stream`.  Returns GEMM_OK, GEMM_ERR_INVALID_ARG (negative extent,
+ * elem_bytes not 2 or 4, leading dimension too small, NULL or misaligned pointer) or
+ * GEMM_ERR_HIP when the launch fails.
+ */
+int gemm_transpose(const void *in, void *out, int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
+                   int32_t elem_bytes, void *stream);
+
 /* gemm_destroy -- release a plan and its workspace.  NULL is ignored. */
 void gemm_destroy(gemm_plan_t plan);
 

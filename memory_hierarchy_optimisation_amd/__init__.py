@@ -40,7 +40,7 @@ DESCRIBE_FIELDS = ("kind", "bm", "bn", "bk", "waves_m", "waves_n", "stages", "sp
 
 EXPORTS = ("gemm_plan", "gemm_plan_config", "gemm_run", "gemm_run_epilogue", "gemm_destroy",
            "gemm_last_error", "gemm_plan_describe", "gemm_catalogue", "gemm_autotune", "gemm_tune_save",
-           "gemm_tune_load", "gemm_tune_clear")
+           "gemm_tune_load", "gemm_tune_clear", "gemm_transpose")
 
 
 class Epilogue(ctypes.Structure):
@@ -101,6 +101,8 @@ def _load():
     lib.gemm_tune_load.restype = i32
     lib.gemm_tune_clear.argtypes = []
     lib.gemm_tune_clear.restype = None
+    lib.gemm_transpose.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp]
+    lib.gemm_transpose.restype = i32
     runtimes = hip_runtimes_mapped()
     if len(runtimes) > 1:
         raise ImportError("more than one HIP runtime is mapped into this process "
@@ -223,3 +225,11 @@ def gemm_tune_load(path):
 
 def gemm_tune_clear():
     _lib.gemm_tune_clear()
+
+
+def gemm_transpose(inp, out, rows, cols, ld_in, ld_out, elem_bytes, stream=None):
+    """out[c * ld_out + r] = inp[r * ld_in + c] for elem_bytes-byte elements (2 or 4)."""
+    rc = _lib.gemm_transpose(_ptr(inp), _ptr(out), rows, cols, ld_in, ld_out, elem_bytes, _stream(stream))
+    if rc != GEMM_OK:
+        raise GemmError(rc, gemm_last_error())
+

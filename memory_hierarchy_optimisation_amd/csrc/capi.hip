@@ -24,6 +24,8 @@ hipError_t launch_big(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_w8(const LaunchArgs &p, int bm, hipStream_t s);
 hipError_t launch_skinny(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_zero_words(void *w, int64_t n, hipStream_t s);
+hipError_t launch_transpose(const void *in, void *out, int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
+                            int elem_bytes, hipStream_t s);
 }  // namespace mhg
 
 struct gemm_plan_s {
@@ -278,6 +280,42 @@ void gemm_destroy(gemm_plan_t plan) {
 }
 
 const char *gemm_last_error(void) { return g_last_error.c_str(); }
+
+int gemm_transpose(const void *in, void *out, int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
+                   int32_t elem_bytes, void *stream) {
+  if (rows < 0 || cols < 0) {
+    set_error("gemm_transpose: negative extent");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (elem_bytes != 2 && elem_bytes != 4) {
+    set_error("gemm_transpose: elem_bytes must be 2 or 4");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (rows == 0 || cols == 0) {
+    set_error("");
+    return GEMM_OK;
+  }
+  if (ld_in < cols || ld_out < rows) {
+    set_error("gemm_transpose: ld_in must be >= cols and ld_out >= rows");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (rows > (int64_t(1) << 31) || cols > (int64_t(1) << 31)) {
+    set_error("gemm_transpose: extents above 2^31 are not supported");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (!in || !out || reinterpret_cast<uintptr_t>(in) % elem_bytes || reinterpret_cast<uintptr_t>(out) % elem_bytes) {
+    set_error("gemm_transpose: NULL or misaligned (not element-aligned) pointer");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  const hipError_t e = mhg::launch_transpose(in, out, rows, cols, ld_in, ld_out, elem_bytes,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_error(std::string("gemm_transpose: launch failed: ") + hipGetErrorString(e));
+    return GEMM_ERR_HIP;
+  }
+  set_error("");
+  return GEMM_OK;
+}
 
 int gemm_plan_describe(gemm_plan_t plan, int32_t out[16]) {
   if (!plan || !out) {

@@ -168,3 +168,21 @@ def epilogue(S, alpha=1.0, beta=0.0, C_prior=None, bias=None, activation="none")
         raise ValueError(f"unknown activation {activation}")
     return T
 
+
+def transpose(x, rows, cols, ld_in, ld_out=None):
+    """The transpose as defined: out[c][r] = in[r][c] ("CUDA tile", applications section,
+    the tiled transpose), element by element over a flat row-major storage of any
+    element type (the values are moved, not interpreted).  Returns the flat output
+    storage (cols x ld_out, padding columns zero)."""
+    x = np.ascontiguousarray(x).reshape(-1)
+    ld_out = rows if ld_out is None else ld_out
+    if ld_in < cols or ld_out < rows:
+        raise ValueError("leading dimension smaller than the row length")
+    if rows and cols and x.size < (rows - 1) * ld_in + cols:
+        raise ValueError("input storage too short")
+    out = np.zeros(cols * ld_out, dtype=x.dtype)
+    r = np.arange(rows, dtype=np.int64)
+    for c in range(cols):
+        out[c * ld_out + r] = x[r * ld_in + c]
+    return out
+

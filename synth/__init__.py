@@ -167,3 +167,13 @@ def epilogue_inputs(M, N, out_t, ldc=None, dist="uniform", seed=1, r=4):
     Cs, _ = lay_out(C, False, ldc)
     return Cs, bias
 
+
+def raw_matrix(rows, ld, elem_bytes, seed=0, pad=0):
+    """rows x ld matrix of random bit patterns of 2- or 4-byte elements (every pattern,
+    NaNs included: a transpose moves bytes), as a CPU tensor of int16 / int32; columns
+    are all drawn, the caller decides how many of them are logical."""
+    gen = torch.Generator().manual_seed(seed)
+    dt = {2: torch.int16, 4: torch.int32}[elem_bytes]
+    lo, hi = (-(1 << 15), 1 << 15) if elem_bytes == 2 else (-(1 << 31), 1 << 31)
+    return torch.randint(lo, hi, (rows, ld), generator=gen, dtype=torch.int64).to(dt)
+

@@ -202,3 +202,15 @@ def test_last_error_clears_on_success():
 def test_one_hip_runtime_in_the_process():
     """The library shares torch's HIP runtime instead of mapping a second one."""
     assert len(mh.hip_runtimes_mapped()) == 1
+
+
+def test_transpose_argument_checks():
+    """gemm_transpose validates before touching a device; empty extents are a no-op."""
+    mh.gemm_transpose(0, 0, 0, 5, 5, 1, 4, stream=0)
+    mh.gemm_transpose(0, 0, 4, 0, 1, 4, 2, stream=0)
+    for args, msg in [((16, 16, 2, 2, 2, 2, 8), "elem_bytes"), ((16, 16, 2, 4, 3, 2, 4), "ld_in"),
+                      ((16, 16, 2, 4, 4, 1, 4), "ld_out"), ((18, 16, 2, 2, 2, 2, 4), "misaligned"),
+                      ((0, 16, 2, 2, 2, 2, 4), "NULL"), ((16, 16, -1, 2, 2, 2, 4), "negative"),
+                      ((16, 16, 1 << 32, 2, 2, 1 << 32, 4), r"2\^31")]:
+        with pytest.raises(mh.GemmError, match=msg):
+            mh.gemm_transpose(*args, stream=0)
