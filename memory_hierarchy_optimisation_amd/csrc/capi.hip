@@ -23,6 +23,7 @@ bool ring_supported(const LaunchArgs &p, int bm, int bn);
 hipError_t launch_big(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_w8(const LaunchArgs &p, int bm, hipStream_t s);
 hipError_t launch_skinny(const LaunchArgs &p, hipStream_t s);
+hipError_t launch_mfma32(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_zero_words(void *w, int64_t n, hipStream_t s);
 hipError_t launch_transpose(const void *in, void *out, int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
                             int elem_bytes, hipStream_t s);
@@ -261,6 +262,8 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
         e = mhg::launch_w8(a, v->cfg.bm, s); break;
       case mhg::L_SKINNY:
         e = mhg::launch_skinny(a, s); break;
+      case mhg::L_MFMA32_128:
+        e = mhg::launch_mfma32(a, s); break;
       default:
         e = mhg::launch_mfma(v->launcher, a, s); break;
     }

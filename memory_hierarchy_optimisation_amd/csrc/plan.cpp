@@ -36,6 +36,8 @@ const Variant kCatalogue[] = {
     // kind            bm   bn   bk  wm wn st sk   thr  types  launcher           tm tn fallback
     {{GEMM_KIND_FMA, 32, 32, 32, 4, 1, 2, 1}, 256, kF32, L_FMA_32, 2, 2, -1},
     {{GEMM_KIND_FMA, 64, 64, 16, 4, 1, 2, 1}, 256, kF32, L_FMA_64, 4, 4, -1},
+    // fp32 on the matrix cores (v_mfma_f32_32x32x2_f32); ahead of the FMA tile of the same size
+    {{GEMM_KIND_MFMA, 128, 128, 16, 2, 2, 2, 1}, 256, kF32, L_MFMA32_128, 4, 4, -1},
     {{GEMM_KIND_FMA, 128, 128, 16, 4, 1, 2, 1}, 256, kF32, L_FMA_128, 8, 8, -1},
     {{GEMM_KIND_MFMA, 64, 64, 128, 2, 4, 5, 1}, 512, kHalf, L_W8_64, 2, 2, L_MFMA_64x64},
     {{GEMM_KIND_MFMA, 64, 64, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_64x64, 2, 2, -1},
@@ -76,6 +78,7 @@ int regs_estimate(const Variant &v) {
   if (v.launcher == L_BIG_256) return 512;   // one wave per SIMD: 256 accumulators in AGPRs
   if (v.launcher == L_W8_256 || v.launcher == L_W8_128 || v.launcher == L_W8_64) return 256;   // two waves per SIMD
   if (v.launcher == L_SKINNY) return 128;    // 8 accumulators, two staged rounds, transposes
+  if (v.launcher == L_MFMA32_128) return 128;   // 64 accumulators, 32 staged, fragments, addressing
   if (is_ring(v.launcher)) {   // accumulators + two fragment sets + addressing
     return v.tm * v.tn * 4 + 2 * (v.tm + v.tn) * 4 + 24;
   }
@@ -129,6 +132,8 @@ double tile_intensity(int bm, int bn, int elem) {
 static int64_t lds_allocated(const Variant &v, int elem) {
   const TileConfig &c = v.cfg;
   if (v.launcher == L_SKINNY) return int64_t(4) * 16 * c.bn * 4 + 16;   // wave partials, flag
+  if (v.launcher == L_MFMA32_128)   // k-rows padded by 32 floats
+    return (int64_t(c.bm + 32) * c.bk + int64_t(c.bn + 32) * c.bk) * elem * c.stages;
   if (c.kind == GEMM_KIND_FMA)
     return (int64_t(c.bm + 4) * c.bk + int64_t(c.bn + 4) * c.bk) * elem * c.stages;
   return lds_bytes_of(c, elem);

@@ -28,6 +28,7 @@ enum LauncherId {
   L_W8_256,
   L_W8_128,
   L_W8_64,
+  L_MFMA32_128,
   L_COUNT
 };
 

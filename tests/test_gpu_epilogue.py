@@ -39,15 +39,23 @@ def _fits(M, N, K, in_t, out_t, cfg):
     return True
 
 
+def _accepts(cfg, in_t):
+    M = 16 if cfg[0] == mh.GEMM_KIND_SKINNY else 512
+    try:
+        p = mh.gemm_plan_config(M, 512, 512, 512, 512, 512, mh.DTYPE_OF[(in_t, "f32")], 0, cfg)
+    except mh.GemmError:
+        return False
+    mh.gemm_destroy(p)
+    return True
+
+
 def _configs():
     out = []
     for c in mh.gemm_catalogue():
-        if c[0] == mh.GEMM_KIND_FMA:
+        if _accepts(c, "f32"):
             out.append((c, "f32", "f32"))
-        elif c[0] == mh.GEMM_KIND_MFMA:
-            out += [(c, "bf16", "bf16"), (c, "f16", "f32")]
-        else:
-            out.append((c, "bf16", "f32"))
+        if _accepts(c, "bf16"):
+            out += [(c, "bf16", "f32")] if c[0] == mh.GEMM_KIND_SKINNY else [(c, "bf16", "bf16"), (c, "f16", "f32")]
     return out
 
 

@@ -45,10 +45,17 @@ def test_catalogue_lists_every_compiled_variant_once():
         assert c[0] in (mh.GEMM_KIND_FMA, mh.GEMM_KIND_MFMA, mh.GEMM_KIND_SKINNY)
         # every listed configuration is accepted by gemm_plan_config for some problem
         M = 16 if c[0] == mh.GEMM_KIND_SKINNY else 512
-        dt = mh.GEMM_F32_F32 if c[0] == mh.GEMM_KIND_FMA else mh.GEMM_BF16_F32
-        p = mh.gemm_plan_config(M, 4096, 4096, 4096, 4096, 4096, dt, 0, c)
-        assert _cfg_of(mh.gemm_plan_describe(p)) == c
-        mh.gemm_destroy(p)
+        taken = 0
+        for dt in (mh.GEMM_F32_F32, mh.GEMM_BF16_F32):
+            try:
+                p = mh.gemm_plan_config(M, 4096, 4096, 4096, 4096, 4096, dt, 0, c)
+            except mh.GemmError as e:
+                assert "input type" in str(e)
+                continue
+            assert _cfg_of(mh.gemm_plan_describe(p)) == c
+            mh.gemm_destroy(p)
+            taken += 1
+        assert taken == 1        # every variant serves exactly one family of input types
 
 
 def test_loaded_choice_overrides_the_heuristic_until_cleared(tmp_path):
