@@ -245,11 +245,14 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
       a.group_m = std::max(1, std::min(a.gm, 4));
       a.split_k = 1;
     }
-    if (v->launcher == mhg::L_SKINNY && a.split_k > 1) {
+    if (a.split_k > 1) {
       const int st = ensure_workspace(plan, s);
       if (st != GEMM_OK) return st;
       a.workspace = plan->ws;
       a.ws_bytes = d.ws_bytes;
+      // Eight-wave split-K: K per chunk, a whole number of slabs.
+      const int64_t bk = v->cfg.bk, per = (d.K + a.split_k - 1) / a.split_k;
+      a.k_chunk = (per + bk - 1) / bk * bk;
     }
     switch (v->launcher) {
       case mhg::L_FMA_32: case mhg::L_FMA_64: case mhg::L_FMA_128:

@@ -318,9 +318,9 @@ struct W8Gemm {
 
   __device__ __forceinline__ uint32_t slot_addr(int t) const { return lds0 + uint32_t(t % SLOTS) * SLOT_BYTES; }
 
-  __device__ __forceinline__ void run(uint32_t lds_base) {
+  __device__ __forceinline__ void run(uint32_t lds_base, int bid) {
     int tm, tn;
-    tile_of(blockIdx.x, p.gm, p.gn, p.group_m, tm, tn);
+    tile_of(bid, p.gm, p.gn, p.group_m, tm, tn);
     m0 = tm * BM;
     n0 = tn * BN;
     lds0 = lds_base;
@@ -614,34 +614,106 @@ struct W8Gemm {
   }
 };
 
-template <class H, bool A_KC, bool B_KC, class TL>
+template <class H, bool A_KC, bool B_KC, class TL, bool SPLIT>
 __global__ void __launch_bounds__(NT)
 w8_gemm(LaunchArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES];
+  const int tiles = p.gm * p.gn;
+  int bid = int(blockIdx.x);
+  if constexpr (SPLIT) {
+    // Split K: workgroup id = z * tiles + tile.  Chunk z of K is the product of A's
+    // columns (B's rows) z * k_chunk .. + k_chunk - 1, computed as a GEMM of its own
+    // into the fp32 partial z of the workspace (M x N, row-major, no epilogue); the
+    // reduction kernel adds the partials in chunk order.
+    const int z = bid / tiles;
+    bid -= z * tiles;
+    const int64_t kb = int64_t(z) * p.k_chunk;
+    p.A = static_cast<const uint16_t *>(p.A) + (A_KC ? kb : kb * p.lda);
+    p.B = static_cast<const uint16_t *>(p.B) + (B_KC ? kb : kb * p.ldb);
+    p.K = p.K - kb < p.k_chunk ? p.K - kb : p.k_chunk;
+    p.C = static_cast<float *>(p.workspace) + int64_t(z) * p.M * p.N;
+    p.ldc = p.N;
+    p.out_code = E_F32;
+    p.c_vec = p.N % 4 == 0;
+    p.epi = 0;
+  }
   W8Gemm<H, A_KC, B_KC, TL> g(p);
-  g.run(uint32_t(size_t((MHG_LDS char *)smem)));
+  g.run(uint32_t(size_t((MHG_LDS char *)smem)), bid);
 }
 
-#define MHG_W8_INST(H, TL)                                            \
-  template __global__ void w8_gemm<H, true, false, TL>(LaunchArgs);  \
-  template __global__ void w8_gemm<H, true, true, TL>(LaunchArgs);   \
-  template __global__ void w8_gemm<H, false, false, TL>(LaunchArgs); \
-  template __global__ void w8_gemm<H, false, true, TL>(LaunchArgs);
-MHG_W8_INST(HalfBF16, Tile256)
-MHG_W8_INST(HalfF16, Tile256)
-MHG_W8_INST(HalfBF16, Tile128)
-MHG_W8_INST(HalfF16, Tile128)
-MHG_W8_INST(HalfBF16, Tile64)
-MHG_W8_INST(HalfF16, Tile64)
+// C = epilogue(sum of the split_k fp32 partials in chunk order): one thread per four
+// consecutive elements of a row of C.  The same partials give the same bits whatever
+// order the chunks' workgroups ran in.
+__global__ void __launch_bounds__(256) splitk_reduce(LaunchArgs p) {
+  const int64_t cpr = (p.N + 3) / 4;   // four-element chunks a row
+  const int64_t q = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (q >= p.M * cpr) return;
+  const int64_t row = q / cpr, col = 4 * (q % cpr), n_in = p.N - col;
+  const float *ws = static_cast<const float *>(p.workspace);
+  const int64_t slice = p.M * p.N, idx = row * p.N + col;
+  const bool vec = p.N % 4 == 0;
+  f32x4 t = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int z = 0; z < p.split_k; ++z) {
+    f32x4 v = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (vec) {
+      v = *reinterpret_cast<const f32x4 *>(ws + z * slice + idx);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (e < n_in) v[e] = ws[z * slice + idx + e];
+    }
+    t = z == 0 ? v : t + v;
+  }
+  if (p.epi) t = epilogue4(p, t, row, col, n_in);
+  store_out4(p.C, row * p.ldc + col, t, p.out_code, p.c_vec && n_in >= 4, int(n_in));
+}
+
+#define MHG_W8_INST(H, TL, SPLIT)                                            \
+  template __global__ void w8_gemm<H, true, false, TL, SPLIT>(LaunchArgs);  \
+  template __global__ void w8_gemm<H, true, true, TL, SPLIT>(LaunchArgs);   \
+  template __global__ void w8_gemm<H, false, false, TL, SPLIT>(LaunchArgs); \
+  template __global__ void w8_gemm<H, false, true, TL, SPLIT>(LaunchArgs);
+MHG_W8_INST(HalfBF16, Tile256, false)
+MHG_W8_INST(HalfF16, Tile256, false)
+MHG_W8_INST(HalfBF16, Tile128, false)
+MHG_W8_INST(HalfF16, Tile128, false)
+MHG_W8_INST(HalfBF16, Tile64, false)
+MHG_W8_INST(HalfF16, Tile64, false)
+// Split-K only where the catalogue has it (the 64 x 64 and 128 x 128 tiles).
+MHG_W8_INST(HalfBF16, Tile128, true)
+MHG_W8_INST(HalfF16, Tile128, true)
+MHG_W8_INST(HalfBF16, Tile64, true)
+MHG_W8_INST(HalfF16, Tile64, true)
 #undef MHG_W8_INST
 
 template <class H, class TL>
 hipError_t launch_typed(const LaunchArgs &p, hipStream_t s) {
-  const dim3 grid(unsigned(p.gm) * unsigned(p.gn)), block(NT);
-  if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL>), grid, block, 0, s, p);
-  else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL>), grid, block, 0, s, p);
-  else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL>), grid, block, 0, s, p);
-  else hipLaunchKernelGGL((w8_gemm<H, false, true, TL>), grid, block, 0, s, p);
+  const int split = p.split_k > 1 ? p.split_k : 1;
+  if (split > 1 && (!p.workspace || p.k_chunk < TL::BK || p.k_chunk % TL::BK ||
+                    p.ws_bytes < int64_t(split) * p.M * p.N * 4))
+    return hipErrorInvalidValue;
+  const dim3 grid(unsigned(p.gm) * unsigned(p.gn) * unsigned(split)), block(NT);
+  if (split == 1) {
+    if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL, false>), grid, block, 0, s, p);
+    else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL, false>), grid, block, 0, s, p);
+    else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((w8_gemm<H, false, true, TL, false>), grid, block, 0, s, p);
+    return hipGetLastError();
+  }
+  if constexpr (TL::BM == 256) {
+    return hipErrorInvalidValue;   // no split-K instantiation of the 256 x 256 tile
+  } else {
+    if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL, true>), grid, block, 0, s, p);
+    else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL, true>), grid, block, 0, s, p);
+    else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL, true>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((w8_gemm<H, false, true, TL, true>), grid, block, 0, s, p);
+  }
+  {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t chunks = p.M * ((p.N + 3) / 4);
+    hipLaunchKernelGGL(splitk_reduce, dim3(unsigned((chunks + 255) / 256)), dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 

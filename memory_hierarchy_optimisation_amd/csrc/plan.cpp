@@ -50,6 +50,14 @@ const Variant kCatalogue[] = {
     {{GEMM_KIND_MFMA, 256, 256, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_256x256_W4, 8, 8, L_MFMA_256x256},
     {{GEMM_KIND_MFMA, 256, 256, 32, 2, 4, 4, 1}, 512, kHalf, L_RING_256x256_W8, 8, 4, L_MFMA_256x256},
     {{GEMM_KIND_MFMA, 256, 256, 64, 2, 4, 2, 1}, 512, kHalf, L_MFMA_256x256, 8, 4, -1},
+    // Eight-wave tiles with K split across workgroups: for grids of tiles that leave
+    // most compute units idle (fp32 partials added in chunk order by a second kernel).
+    {{GEMM_KIND_MFMA, 64, 64, 128, 2, 4, 5, 2}, 512, kHalf, L_W8_64, 2, 2, L_MFMA_64x64},
+    {{GEMM_KIND_MFMA, 64, 64, 128, 2, 4, 5, 4}, 512, kHalf, L_W8_64, 2, 2, L_MFMA_64x64},
+    {{GEMM_KIND_MFMA, 64, 64, 128, 2, 4, 5, 8}, 512, kHalf, L_W8_64, 2, 2, L_MFMA_64x64},
+    {{GEMM_KIND_MFMA, 128, 128, 64, 2, 4, 5, 2}, 512, kHalf, L_W8_128, 4, 4, L_MFMA_128x128},
+    {{GEMM_KIND_MFMA, 128, 128, 64, 2, 4, 5, 4}, 512, kHalf, L_W8_128, 4, 4, L_MFMA_128x128},
+    {{GEMM_KIND_MFMA, 128, 128, 64, 2, 4, 5, 8}, 512, kHalf, L_W8_128, 4, 4, L_MFMA_128x128},
     // M <= 16: one workgroup per 128 columns and K chunk (split-K factor last).
     {{GEMM_KIND_SKINNY, 16, 128, 32, 1, 4, 2, 1}, 256, kHalf, L_SKINNY, 1, 8, L_MFMA_64x64},
     {{GEMM_KIND_SKINNY, 16, 128, 32, 1, 4, 2, 2}, 256, kHalf, L_SKINNY, 1, 8, L_MFMA_64x64},
@@ -245,6 +253,10 @@ int skinny_split(const PlanData &p, const Hardware &hw) {
 double score(const Variant &v, const PlanData &p, const Hardware &hw, std::string *why) {
   const int elem = elem_bytes(p.in_code);
   if (v.launcher == L_SKINNY && !skinny_shape_ok(p, why)) return -1.0;
+  if (v.launcher != L_SKINNY && v.cfg.split_k > 1 && p.K < int64_t(2) * v.cfg.split_k * v.cfg.bk) {
+    if (why) *why = "split-K variant needs at least two K slabs per chunk";
+    return -1.0;
+  }
   if (v.launcher == L_BIG_256 && (p.layout & GEMM_A_COL)) {
     if (why) *why = "256x256 four-wave variant needs row-major A";
     return -1.0;
@@ -301,6 +313,8 @@ static void fill_plan(PlanData *p, int idx, const Hardware &hw) {
   p->ws_bytes = 0;
   if (v.launcher == L_SKINNY && v.cfg.split_k > 1)   // arrival counters, then partials
     p->ws_bytes = (int64_t(p->gn) * 4 + 255) / 256 * 256 + int64_t(v.cfg.split_k) * p->gn * 16 * v.cfg.bn * 4;
+  if (v.launcher != L_SKINNY && v.cfg.split_k > 1)   // one fp32 partial of C per K chunk
+    p->ws_bytes = int64_t(v.cfg.split_k) * p->M * p->N * 4;
 }
 
 bool select(PlanData *p, const Hardware &hw, std::string *err) {
@@ -329,7 +343,7 @@ bool select(PlanData *p, const Hardware &hw, std::string *err) {
   int best = -1;
   double best_score = -1.0;
   for (int i = 0; i < n; ++i) {
-    if (cat[i].launcher == L_SKINNY) continue;
+    if (cat[i].launcher == L_SKINNY || cat[i].cfg.split_k > 1) continue;
     double s = score(cat[i], *p, hw, nullptr);
     if (s > best_score + 1e-12) {
       best_score = s;
@@ -339,6 +353,21 @@ bool select(PlanData *p, const Hardware &hw, std::string *err) {
   if (best < 0 || best_score <= 0.0) {
     *err = "gemm_plan: no compiled variant fits this problem";
     return false;
+  }
+  // Too few workers ("GPU Kernel 的 Tile、Grid、Wave 与 Launch Overhead", per-shape
+  // section): when the chosen eight-wave tile's grid covers at most half the compute
+  // units, K is split across workgroups as well, by the smallest power of two that
+  // fills them, keeping at least four K slabs per chunk.
+  const Variant &b = cat[best];
+  const int64_t tiles = ((p->M + b.cfg.bm - 1) / b.cfg.bm) * ((p->N + b.cfg.bn - 1) / b.cfg.bn);
+  if ((b.launcher == L_W8_64 || b.launcher == L_W8_128) && 2 * tiles <= hw.cus) {
+    int split = 1;
+    while (split < 8 && tiles * split < hw.cus && p->K >= int64_t(4) * (2 * split) * b.cfg.bk) split *= 2;
+    for (int i = 0; split > 1 && i < n; ++i)
+      if (cat[i].launcher == b.launcher && cat[i].cfg.split_k == split && score(cat[i], *p, hw, nullptr) >= 0.0) {
+        best = i;
+        break;
+      }
   }
   fill_plan(p, best, hw);
   return true;

@@ -93,6 +93,7 @@ struct LaunchArgs {
   int group_m;        // rows of tiles walked together (L2 locality)
   void *workspace;
   int64_t ws_bytes;
+  int64_t k_chunk;     // split-K of the eight-wave kernels: K per chunk (a multiple of BK)
   // Fused epilogue, C = act(alpha * product + beta * prior C + bias[column]); epi = 0 is
   // the plain product (alpha 1, beta 0, no bias, no activation) and skips all of it.
   int epi;

@@ -63,6 +63,8 @@ def _configs():
 def test_every_variant_with_bias_relu_alpha_beta(cfg, in_t, out_t):
     if cfg[0] == mh.GEMM_KIND_SKINNY:
         M, N, K = 16, 1096, 1032
+    elif cfg[7] > 1:     # eight-wave split-K: two K slabs a chunk at least
+        M, N, K = 304, 272, 2 * cfg[7] * cfg[3] + 40
     else:
         M, N, K = (300, 270, 200) if _fits(300, 270, 200, in_t, out_t, cfg) else (304, 272, 200)
     print(f"[epilogue variant {cfg} {in_t}->{out_t}] M={M} N={N} K={K}", flush=True)

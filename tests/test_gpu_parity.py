@@ -40,8 +40,8 @@ def _accepts(cfg, in_t):
 
 def _catalogue_for(in_t):
     """Every compiled tile configuration for an input type (the library's catalogue,
-    without the M <= 16 split-K variants, which have tests of their own)."""
-    return [c for c in mh.gemm_catalogue() if c[0] != mh.GEMM_KIND_SKINNY and _accepts(c, in_t)]
+    without the split-K variants, which have tests of their own)."""
+    return [c for c in mh.gemm_catalogue() if c[0] != mh.GEMM_KIND_SKINNY and c[7] == 1 and _accepts(c, in_t)]
 
 
 # ---- the measured workloads at full size ---------------------------------------------------
