@@ -216,13 +216,13 @@ def test_transpose_argument_checks():
             mh.gemm_transpose(*args, stream=0)
 
 
-@pytest.mark.parametrize("M,N,K,split", [(512, 512, 8192, 4), (256, 256, 16384, 8), (768, 512, 4096, 4),
+@pytest.mark.parametrize("M,N,K,split", [(512, 512, 8192, 4), (256, 256, 16384, 8), (768, 512, 4096, 2),
                                          (512, 512, 512, 1), (1024, 1024, 1024, 1), (4096, 4096, 4096, 1)])
 def test_eight_wave_split_k_for_small_grids(M, N, K, split):
     """Too few workers: a grid of eight-wave tiles that covers at most half of the 256
-    compute units gets K split by the smallest power of two (at most 8) that fills
-    them, with at least four K slabs per chunk; the plan then owns split x M x N fp32
-    partials."""
+    compute units gets K split by the smallest power of two (at most 8) that covers
+    three quarters of them, with at least four K slabs per chunk; the plan then owns
+    split x M x N fp32 partials."""
     d = _plan(M, N, K, mh.GEMM_BF16_BF16)
     assert d["split_k"] == split and d["grid_z"] == split
     assert d["workspace_bytes"] == (split * M * N * 4 if split > 1 else 0)
