@@ -79,7 +79,8 @@ __device__ __forceinline__ void tile_of(int bid, int gm, int gn, int group_m, in
 // Store four consecutive elements C[idx .. idx+3] from fp32 values, converting to the
 // output type (round to nearest even).  `vec`: the four are inside the matrix and the
 // address is aligned for one 8-byte (16-bit types) or 16-byte (fp32) store; otherwise
-// element `e` is stored only when e < n_in.
+// element `e` is stored only when e < n_in.  (Ordinary stores: streaming ones here
+// measured slower, 1024^3 f16 9.0 -> 10.8 us.)
 __device__ __forceinline__ void store_out4(void *C, int64_t idx, f32x4 v, int out_code, bool vec, int n_in) {
   if (out_code == E_F32) {
     float *c = reinterpret_cast<float *>(C) + idx;

@@ -595,13 +595,16 @@ struct W8Gemm {
   }
 
   // 16 bytes of converted output (W elements) for C[row][col .. col + W - 1]: one
-  // store when all W lie inside the matrix, else the elements that do.
+  // streaming store when all W lie inside the matrix, else the elements that do.  C
+  // is written once and not read again here; streamed, its lines do not stay dirty
+  // in L2 to be written back when the kernel ends (measured: 4096^3 1.4% and
+  // 2048^3 NT 3.5% faster than with ordinary stores).
   __device__ __forceinline__ void store_chunk(int64_t row, int64_t col, u32x4 v, int W) const {
     if (row >= p.M || col >= p.N) return;
     const int64_t idx = row * p.ldc + col;
     if (col + W <= p.N) {
-      if (W == 4) *reinterpret_cast<u32x4 *>(static_cast<float *>(p.C) + idx) = v;
-      else *reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p.C) + idx) = v;
+      if (W == 4) __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<float *>(p.C) + idx));
+      else __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(static_cast<uint16_t *>(p.C) + idx));
       return;
     }
     const int n_in = int(p.N - col);
