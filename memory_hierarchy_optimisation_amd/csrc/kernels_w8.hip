@@ -202,13 +202,16 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 #define MHG_ORDER() __builtin_amdgcn_sched_barrier(0)
 
-template <class H, bool A_KC, bool B_KC, class TL>
+// PRIOR (256 x 256 only): the fused epilogue reads a 16-bit prior C, which arrives in
+// LDS through the ring's last four slab loads.
+template <class H, bool A_KC, bool B_KC, class TL, bool PRIOR>
 struct W8Gemm {
   static constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, FM = TL::FM, FN = TL::FN;
   static constexpr bool ALT = TL::KSPLIT == 2;           // groups take alternate slabs
   static constexpr int STEPS = BK / 16;                  // 16-deep steps of a slab
   static constexpr int WTM = 32 * FM, WTN = 32 * FN;      // a wave's block of C
   static_assert(BM * BK * 2 == OP_BYTES && BN * BK * 2 == OP_BYTES, "slab size");
+  static_assert(!PRIOR || (!ALT && FM == 4 && FN == 2), "prior C through LDS: 256 x 256 tile only");
 
   const LaunchArgs &p;
   int m0, n0;
@@ -265,7 +268,8 @@ struct W8Gemm {
   // loads 2 S and 2 S + 1 of the group's operand after reads 1 and T / 2 + 1 (T >= 6,
   // so both exist).  Groups on alternate slabs: load S of A after read 0 and load S of
   // B after read 1, for the first LOADS steps (T >= 2).
-  template <int S, int K>
+  // PAST: slab t + 4 lies past K (the last four slabs of the 256 x 256 loop).
+  template <int S, int K, bool PAST>
   __device__ __forceinline__ void reads_from(uint32_t slot, int t) {
     if constexpr (K < T) {
       read<S, K>(slot); MHG_ORDER();
@@ -274,10 +278,11 @@ struct W8Gemm {
         const int k0 = (t + AHEAD) * BK;
         const uint32_t dst = slot_addr(t + AHEAD);
         if constexpr (ALT) (K == 0 ? ld : ld2).issue(k0, kdim - k0, dst, gw, S);
+        else if constexpr (PAST) load(t + AHEAD, dst, 2 * S + (K != 1));
         else ld.issue(k0, kdim - k0, dst, gw, 2 * S + (K != 1));
         MHG_ORDER();
       }
-      reads_from<S, K + 1>(slot, t);
+      reads_from<S, K + 1, PAST>(slot, t);
     }
   }
   // Every load of slab t this wave makes (prologue).
@@ -285,20 +290,48 @@ struct W8Gemm {
     const int k0 = t * BK;
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      ld.issue(k0, kdim - k0, slot_addr(t), gw, j);
-      if (ALT) ld2.issue(k0, kdim - k0, slot_addr(t), gw, j);
+      if (ALT) {
+        ld.issue(k0, kdim - k0, slot_addr(t), gw, j);
+        ld2.issue(k0, kdim - k0, slot_addr(t), gw, j);
+      } else {
+        load(t, slot_addr(t), j);
+      }
     }
+  }
+
+  // Load j of the group's operand of slab t (256 x 256).  The four slabs past K would
+  // load zeros; with the prior C in LDS (PRIOR), slab KT + q loads quarter q of
+  // the tile's prior C instead: rows 64 q .. 64 q + 63, group g the 32 rows from
+  // 64 q + 32 g, into the same half of the same slot and with the same number of loads,
+  // so the ring's waits do not change.  A half is 32 rows of 512 bytes; the 16-byte
+  // chunk c (columns 8 c .. 8 c + 7) of row r sits at 16 (c ^ pswz(r)).
+  static __device__ __forceinline__ int pswz(int r) { return ((r >> 1) & 7) | ((r & 1) << 3); }
+  __device__ __forceinline__ void load(int t, uint32_t dst, int j) const {
+    const int k0 = t * BK;
+    if (!PRIOR || k0 < kdim) {
+      ld.issue(k0, kdim - k0, dst, gw, j);
+      return;
+    }
+    const int q = t - (kdim + BK - 1) / BK;
+    const int64_t row0 = int64_t(m0) + 64 * q + 32 * int(grp);
+    const int lane = threadIdx.x & 63, b = GROUP * j + int(gw);
+    const int r = 2 * b + (lane >> 5), c = (lane & 31) ^ pswz(r);
+    const bool in = row0 + r < p.M && n0 + 8 * c < p.N;
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(static_cast<const uint16_t *>(p.C) + row0 * p.ldc + n0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MHG_LDS void *)(size_t)(dst + ld.lds_off + b * 1024), 16,
+                                             in ? uint32_t((int64_t(r) * p.ldc + 8 * c) * 2) : kOut, 0, 0, 0);
   }
 
   // Memory phase for slab t: read all of the wave's fragments of slab t and request
   // loads of slab t+4 (into the slot of slab t-1, which every wave has finished
   // reading: the last reader ended its phase with every read complete).
-  template <int S>
+  template <int S, bool PAST>
   __device__ __forceinline__ void mem_steps(uint32_t slot, int t) {
-    if constexpr (S < STEPS) { reads_from<S, 0>(slot, t); mem_steps<S + 1>(slot, t); }
+    if constexpr (S < STEPS) { reads_from<S, 0, PAST>(slot, t); mem_steps<S + 1, PAST>(slot, t); }
   }
+  template <bool PAST = false>
   __device__ __forceinline__ void mem(int t) {
-    mem_steps<0>(slot_addr(t), t);
+    mem_steps<0, PAST>(slot_addr(t), t);
     wait_lgkm<0>();
     MHG_ORDER();
   }
@@ -376,8 +409,21 @@ struct W8Gemm {
       barrier();
       if (grp == 1) barrier();
       MHG_ORDER();
-      for (int t = 0; t < KT; ++t) {
+      // The last four iterations request the slabs past K; a loop of their own keeps
+      // the choice of what those load (zeros, or the prior C) out of the main loop.
+      int t = 0;
+      for (; t < KT - AHEAD; ++t) {
         mem(t);
+        wait_vm<3 * LOADS>();
+        barrier();
+        MHG_ORDER();
+        compute();
+        wait_vm<3 * LOADS>();
+        barrier();
+        MHG_ORDER();
+      }
+      for (; t < KT; ++t) {
+        mem<true>(t);
         wait_vm<3 * LOADS>();
         barrier();
         MHG_ORDER();
@@ -457,6 +503,10 @@ struct W8Gemm {
   __device__ __forceinline__ void epilogue(int lane, uint32_t region) {
     const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
     const int ob = p.out_code == E_F32 ? 4 : 2;
+    if constexpr (PRIOR) {
+      epilogue_prior(lane);
+      return;
+    }
     // Staging is laid out for 64-column blocks of 64 or 128 rows; the 32 x 32 blocks of
     // the 64 x 64 tile (2 KiB of C a wave) store directly.
     constexpr bool STAGE = FN == 2 && FM % 2 == 0;
@@ -594,6 +644,58 @@ struct W8Gemm {
     }
   }
 
+  // The epilogue with the prior C (16-bit) already in LDS, quarter q of the tile in the
+  // slot of slab KT + q.  Each lane combines its accumulators with the prior values at
+  // the same places and writes the rounded results over them (one lane per place); the
+  // wave then stores its 128 x 64 block from there in 128-byte row pieces.  Rows and
+  // columns outside C were loaded as zeros and are not stored.
+  __device__ __forceinline__ uint32_t prior_at(int R, int c) const {
+    const int KT = (kdim + BK - 1) / BK, r = R & 31;
+    return slot_addr(KT + R / 64) + uint32_t((R >> 5) & 1) * OP_BYTES + uint32_t(r * 512 + 16 * (c ^ pswz(r)));
+  }
+  __device__ __forceinline__ void epilogue_prior(int lane) {
+    const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
+    const int colL = wn * WTN + 4 * (lane >> 5);          // tile column of the lane's first piece
+    f32x4 b[FN][4];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t col = n0 + colL + 32 * j + 8 * q;
+        b[j][q] = col < p.N ? bias4(p, col, p.N - col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int R = wm * WTM + 32 * i + (lane & 31), Cc = colL + 32 * j + 8 * q;
+          MHG_LDS u32x2 *at = reinterpret_cast<MHG_LDS u32x2 *>(size_t(prior_at(R, Cc >> 3) + 8 * ((Cc >> 2) & 1)));
+          const u32x2 h = *at;
+          f32x4 c;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint16_t u = uint16_t(h[e >> 1] >> (16 * (e & 1)));
+            c[e] = p.out_code == E_F16 ? float(__builtin_bit_cast(_Float16, u)) : float(__builtin_bit_cast(__bf16, u));
+          }
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          const f32x4 f = epilogue4pb(p, v, c, b[j][q], 4);
+          uint16_t o[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            o[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)f[e]) : __builtin_bit_cast(uint16_t, (__bf16)f[e]);
+          *at = u32x2{uint32_t(o[0]) | (uint32_t(o[1]) << 16), uint32_t(o[2]) | (uint32_t(o[3]) << 16)};
+          MHG_ORDER();     // one piece at a time: hoisting every read would spill
+        }
+#pragma unroll
+    for (int k = 0; k < WTM / 8; ++k) {
+      const int rr = 8 * k + (lane >> 3), cc = lane & 7;
+      const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(prior_at(wm * WTM + rr, wn * (WTN / 8) + cc)));
+      store_chunk(rowW + rr, colW + 8 * cc, v, 8);
+    }
+  }
+
   // 16 bytes of converted output (W elements) for C[row][col .. col + W - 1]: one
   // streaming store when all W lie inside the matrix, else the elements that do.  C
   // is written once and not read again here; streamed, its lines do not stay dirty
@@ -617,7 +719,7 @@ struct W8Gemm {
   }
 };
 
-template <class H, bool A_KC, bool B_KC, class TL, bool SPLIT>
+template <class H, bool A_KC, bool B_KC, class TL, bool SPLIT, bool PRIOR>
 __global__ void __launch_bounds__(NT)
 w8_gemm(LaunchArgs p) {
   __shared__ __attribute__((aligned(1024))) char smem[SLOTS * SLOT_BYTES];
@@ -640,7 +742,7 @@ w8_gemm(LaunchArgs p) {
     p.c_vec = p.N % 4 == 0;
     p.epi = 0;
   }
-  W8Gemm<H, A_KC, B_KC, TL> g(p);
+  W8Gemm<H, A_KC, B_KC, TL, PRIOR> g(p);
   g.run(uint32_t(size_t((MHG_LDS char *)smem)), bid);
 }
 
@@ -671,22 +773,25 @@ __global__ void __launch_bounds__(256) splitk_reduce(LaunchArgs p) {
   store_out4(p.C, row * p.ldc + col, t, p.out_code, p.c_vec && n_in >= 4, int(n_in));
 }
 
-#define MHG_W8_INST(H, TL, SPLIT)                                            \
-  template __global__ void w8_gemm<H, true, false, TL, SPLIT>(LaunchArgs);  \
-  template __global__ void w8_gemm<H, true, true, TL, SPLIT>(LaunchArgs);   \
-  template __global__ void w8_gemm<H, false, false, TL, SPLIT>(LaunchArgs); \
-  template __global__ void w8_gemm<H, false, true, TL, SPLIT>(LaunchArgs);
-MHG_W8_INST(HalfBF16, Tile256, false)
-MHG_W8_INST(HalfF16, Tile256, false)
-MHG_W8_INST(HalfBF16, Tile128, false)
-MHG_W8_INST(HalfF16, Tile128, false)
-MHG_W8_INST(HalfBF16, Tile64, false)
-MHG_W8_INST(HalfF16, Tile64, false)
+#define MHG_W8_INST(H, TL, SPLIT, PRIOR)                                            \
+  template __global__ void w8_gemm<H, true, false, TL, SPLIT, PRIOR>(LaunchArgs);  \
+  template __global__ void w8_gemm<H, true, true, TL, SPLIT, PRIOR>(LaunchArgs);   \
+  template __global__ void w8_gemm<H, false, false, TL, SPLIT, PRIOR>(LaunchArgs); \
+  template __global__ void w8_gemm<H, false, true, TL, SPLIT, PRIOR>(LaunchArgs);
+MHG_W8_INST(HalfBF16, Tile256, false, false)
+MHG_W8_INST(HalfF16, Tile256, false, false)
+MHG_W8_INST(HalfBF16, Tile128, false, false)
+MHG_W8_INST(HalfF16, Tile128, false, false)
+MHG_W8_INST(HalfBF16, Tile64, false, false)
+MHG_W8_INST(HalfF16, Tile64, false, false)
 // Split-K only where the catalogue has it (the 64 x 64 and 128 x 128 tiles).
-MHG_W8_INST(HalfBF16, Tile128, true)
-MHG_W8_INST(HalfF16, Tile128, true)
-MHG_W8_INST(HalfBF16, Tile64, true)
-MHG_W8_INST(HalfF16, Tile64, true)
+MHG_W8_INST(HalfBF16, Tile128, true, false)
+MHG_W8_INST(HalfF16, Tile128, true, false)
+MHG_W8_INST(HalfBF16, Tile64, true, false)
+MHG_W8_INST(HalfF16, Tile64, true, false)
+// The 256 x 256 tile with the prior C through LDS.
+MHG_W8_INST(HalfBF16, Tile256, false, true)
+MHG_W8_INST(HalfF16, Tile256, false, true)
 #undef MHG_W8_INST
 
 template <class H, class TL>
@@ -697,19 +802,33 @@ hipError_t launch_typed(const LaunchArgs &p, hipStream_t s) {
     return hipErrorInvalidValue;
   const dim3 grid(unsigned(p.gm) * unsigned(p.gn) * unsigned(split)), block(NT);
   if (split == 1) {
-    if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL, false>), grid, block, 0, s, p);
-    else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL, false>), grid, block, 0, s, p);
-    else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL, false>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((w8_gemm<H, false, true, TL, false>), grid, block, 0, s, p);
+    // The 256 x 256 tile brings a 16-bit prior C into LDS with its last slab loads when
+    // C's rows are whole 16-byte chunks (aligned base, ldc and N multiples of 8) and a
+    // half-quarter (32 rows) spans less than 2^31 bytes.
+    const bool prior = p.epi && p.beta != 0.0f && p.out_code != E_F32 && p.N % 8 == 0 && p.ldc % 8 == 0 &&
+                       p.ldc < (int64_t(1) << 24) && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
+    if constexpr (TL::BM == 256) {
+      if (prior) {
+        if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL, false, true>), grid, block, 0, s, p);
+        else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL, false, true>), grid, block, 0, s, p);
+        else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL, false, true>), grid, block, 0, s, p);
+        else hipLaunchKernelGGL((w8_gemm<H, false, true, TL, false, true>), grid, block, 0, s, p);
+        return hipGetLastError();
+      }
+    }
+    if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL, false, false>), grid, block, 0, s, p);
+    else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL, false, false>), grid, block, 0, s, p);
+    else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL, false, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((w8_gemm<H, false, true, TL, false, false>), grid, block, 0, s, p);
     return hipGetLastError();
   }
   if constexpr (TL::BM == 256) {
     return hipErrorInvalidValue;   // no split-K instantiation of the 256 x 256 tile
   } else {
-    if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL, true>), grid, block, 0, s, p);
-    else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL, true>), grid, block, 0, s, p);
-    else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL, true>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((w8_gemm<H, false, true, TL, true>), grid, block, 0, s, p);
+    if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL, true, false>), grid, block, 0, s, p);
+    else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL, true, false>), grid, block, 0, s, p);
+    else if (p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, false, false, TL, true, false>), grid, block, 0, s, p);
+    else hipLaunchKernelGGL((w8_gemm<H, false, true, TL, true, false>), grid, block, 0, s, p);
   }
   {
     const hipError_t e = hipGetLastError();

@@ -183,3 +183,48 @@ def test_workloads_with_epilogue(name):
                         w.dtype, ii, jj, a_col=w.a_col, b_col=w.b_col)
     ref = oracle.epilogue(S[None, :], 0.5, 0.25, Cp[ii, jj][None, :], bias.numpy()[jj], "relu")[0]
     check_tolerance(vals[ii, jj], ref, w.out, f"{name} sampled")
+
+
+# The 256 x 256 eight-wave tile brings a 16-bit prior C into LDS with the loads of the
+# four slabs past K (in the prologue when K has fewer than four slabs); these cases
+# cover every slab count up to nine, ragged tiles, a padded C and the launches that
+# fall back to the staged path (C misaligned, N not a multiple of 8).
+CFG256 = (2, 256, 256, 32, 2, 4, 5, 1)
+
+
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 160, 200, 224, 288])
+@pytest.mark.parametrize("in_t", ["f16", "bf16"])
+def test_256_tile_prior_c_every_slab_count(K, in_t):
+    M, N = 264, 520
+    a_col = b_col = K % 64 == 0
+    print(f"[epilogue 256 prior {in_t} K={K} layout={a_col}]", flush=True)
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col=a_col, b_col=b_col, dist="int", r=3, seed=K)
+    Cs, bias = synth.epilogue_inputs(M, N, in_t, dist="int", r=4, seed=K + 1)
+    epi = dict(alpha=2.0, beta=-1.0, bias=bias, activation=mh.GEMM_ACT_RELU)
+    _, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, in_t, a_col, b_col, cfg=CFG256, c_init=Cs, epi=epi)
+    assert (desc["bm"], desc["bn"]) == (256, 256)
+    S = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
+    check_exact(raw, _reference(S, Cs, bias, in_t, epi, N), in_t, f"K={K}")
+
+
+@pytest.mark.parametrize("case", ["padded_ldc", "misaligned_c", "n_not_multiple_of_8", "no_bias_beta_only"])
+def test_256_tile_prior_c_layouts_and_fallbacks(case):
+    in_t = "bf16"
+    M, N, K, ldc, off_c, b_col = 300, 264, 136, None, 0, False
+    epi_kw = dict(alpha=0.5, beta=1.5, activation=mh.GEMM_ACT_NONE)
+    if case == "padded_ldc":
+        ldc = N + 24
+    elif case == "misaligned_c":
+        off_c = 1
+    elif case == "n_not_multiple_of_8":
+        N, b_col = 262, True
+    print(f"[epilogue 256 prior {case}] M={M} N={N} K={K} ldc={ldc} off_c={off_c}", flush=True)
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, b_col=b_col, dist="int", r=3, seed=21)
+    Cs, bias = synth.epilogue_inputs(M, N, in_t, dist="int", r=4, seed=22)
+    epi = dict(epi_kw, bias=None if case == "no_bias_beta_only" else bias)
+    _, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, in_t, False, b_col, ldc=ldc, offset_c=off_c, cfg=CFG256,
+                        c_init=Cs, epi=epi)
+    S = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, False, b_col)
+    ref_bias = np.zeros(N, np.float32) if epi["bias"] is None else bias.numpy()[:N]
+    ref = oracle.epilogue(S, epi["alpha"], epi["beta"], _prior(Cs, in_t)[:, :N], ref_bias, "none")
+    check_exact(raw, ref, in_t, case)

@@ -66,7 +66,7 @@ def _mfma_loops(lines):
 
 
 @pytest.mark.parametrize("src,prefix,n_kernels", [
-    ("kernels_w8.hip", "_ZN3mhg2w87w8_gemm", 40),
+    ("kernels_w8.hip", "_ZN3mhg2w87w8_gemm", 48),
     ("kernels_skinny.hip", "_ZN3mhg6skinny11skinny_gemm", 2),
 ])
 def test_hot_loops_have_no_lane_loops_and_no_scratch(src, prefix, n_kernels, asm):
