@@ -805,9 +805,9 @@ hipError_t launch_typed(const LaunchArgs &p, hipStream_t s) {
     // The 256 x 256 tile brings a 16-bit prior C into LDS with its last slab loads when
     // C's rows are whole 16-byte chunks (aligned base, ldc and N multiples of 8) and a
     // half-quarter (32 rows) spans less than 2^31 bytes.
-    const bool prior = p.epi && p.beta != 0.0f && p.out_code != E_F32 && p.N % 8 == 0 && p.ldc % 8 == 0 &&
-                       p.ldc < (int64_t(1) << 24) && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
     if constexpr (TL::BM == 256) {
+      const bool prior = p.epi && p.beta != 0.0f && p.out_code != E_F32 && p.N % 8 == 0 && p.ldc % 8 == 0 &&
+                         p.ldc < (int64_t(1) << 24) && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
       if (prior) {
         if (!p.a_col && !p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, false, TL, false, true>), grid, block, 0, s, p);
         else if (!p.a_col && p.b_col) hipLaunchKernelGGL((w8_gemm<H, true, true, TL, false, true>), grid, block, 0, s, p);
