@@ -389,7 +389,9 @@ def main():
                 f"{100 * r['frac_of_roofline']:.1f}% of the {r['bound']} roofline, tile {r['tile']}")
     extras = {}
     if not args.no_per_shape and not args.no_extras:
-        r = measure(args.workload, 100, 20, per_call=True, epilogue=True)
+        # The same warm-up as the headline: the clock settles again after the smaller
+        # per-shape lines, and the timed calls should see the steady state.
+        r = measure(args.workload, 100, args.warmup, per_call=True, epilogue=True)
         extras["epilogue"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         log(f"[bench] {r['workload']} (alpha, beta = 1, bias, ReLU): {r['kernel_tflops']:.1f} TFLOP/s, "
             f"kernel {r['kernel_ms_event'] * 1000:.1f} us against {head['kernel_ms_event'] * 1000:.1f} us plain")
