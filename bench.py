@@ -383,7 +383,9 @@ def main():
     shapes = []
     if not args.no_per_shape:
         for name in PER_SHAPE:
-            r = head if name == args.workload else measure(name, 100, 10, per_call=True)
+            # Small shapes too get a few hundred untimed calls first: the clock that the
+            # previous line left is not the one a steady stream of these calls settles to.
+            r = head if name == args.workload else measure(name, 300, 300, per_call=True)
             shapes.append(r)
             log(f"[bench] {name}: {r['kernel_tflops']:.1f} TFLOP/s, {r['kernel_gbps']:.0f} GB/s, "
                 f"{100 * r['frac_of_roofline']:.1f}% of the {r['bound']} roofline, tile {r['tile']}")
