@@ -48,6 +48,13 @@
 // range and arrive as zeros ("CUDA tile", 4: zero is the identity of the sum); stores
 // are masked.  The host requires 16-byte aligned operands whose contiguous extents and
 // leading dimensions are multiples of 8 elements.
+//
+// Output: the accumulators go through LDS once the ring is free, so that every store
+// writes whole row segments of C (streaming stores: C is written once).  A fused
+// epilogue (alpha, beta times the prior C, bias, ReLU) runs there in fp32 before the
+// one rounding.  The 256 x 256 tile has a second instantiation for a 16-bit prior C:
+// the four slab requests past K load the prior C tile into the ring instead of zeros,
+// so its reads overlap the last slabs' arithmetic.
 #include "device.h"
 
 namespace mhg {
