@@ -368,8 +368,8 @@ def main():
                           os.path.join(ROOT, "profiles", f"traffic_{args.workload}.txt"))
         return
     if args.gpus != 1:
-        log(f"bench.py measures one GPU: this build runs the product on a single MI355X "
-            f"(--gpus {args.gpus} is not supported)")
+        log(f"bench.py measures one GPU: the product runs on a single MI355X, and sharding it over "
+            f"several GPUs is a design note, not code (--gpus {args.gpus} is not supported)")
         sys.exit(2)
 
     import torch
