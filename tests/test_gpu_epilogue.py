@@ -228,3 +228,16 @@ def test_256_tile_prior_c_layouts_and_fallbacks(case):
     ref_bias = np.zeros(N, np.float32) if epi["bias"] is None else bias.numpy()[:N]
     ref = oracle.epilogue(S, epi["alpha"], epi["beta"], _prior(Cs, in_t)[:, :N], ref_bias, "none")
     check_exact(raw, ref, in_t, case)
+
+
+@pytest.mark.parametrize("in_t", ["f16", "bf16"])
+@pytest.mark.parametrize("a_col,b_col", [(False, False), (False, True), (True, False), (True, True)])
+def test_256_tile_prior_c_every_layout(in_t, a_col, b_col):
+    M, N, K = 520, 264, 136
+    print(f"[epilogue 256 prior layout {in_t} a_col={a_col} b_col={b_col}]", flush=True)
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col=a_col, b_col=b_col, dist="int", r=3, seed=41)
+    Cs, bias = synth.epilogue_inputs(M, N, in_t, dist="int", r=4, seed=42)
+    epi = dict(alpha=-1.0, beta=0.5, bias=bias, activation=mh.GEMM_ACT_RELU)
+    _, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, in_t, a_col, b_col, cfg=CFG256, c_init=Cs, epi=epi)
+    S = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
+    check_exact(raw, _reference(S, Cs, bias, in_t, epi, N), in_t, f"layout {a_col},{b_col}")
