@@ -271,25 +271,12 @@ struct W8Gemm {
       }
     }
   }
-  // Reads K .. T-1 of step S, interleaved with the loads of slab t + 4.  256 x 256:
-  // loads 2 S and 2 S + 1 of the group's operand after reads 1 and T / 2 + 1 (T >= 6,
-  // so both exist).  Groups on alternate slabs: load S of A after read 0 and load S of
-  // B after read 1, for the first LOADS steps (T >= 2).
-  // PAST: slab t + 4 lies past K (the last four slabs of the 256 x 256 loop).
-  template <int S, int K, bool PAST>
-  __device__ __forceinline__ void reads_from(uint32_t slot, int t) {
+  // Reads K .. T-1 of step S, back to back.
+  template <int S, int K>
+  __device__ __forceinline__ void reads_from(uint32_t slot) {
     if constexpr (K < T) {
       read<S, K>(slot); MHG_ORDER();
-      constexpr bool load_here = ALT ? (S < LOADS && K < 2) : (K == 1 || K == T / 2 + 1);
-      if constexpr (load_here) {
-        const int k0 = (t + AHEAD) * BK;
-        const uint32_t dst = slot_addr(t + AHEAD);
-        if constexpr (ALT) (K == 0 ? ld : ld2).issue(k0, kdim - k0, dst, gw, S);
-        else if constexpr (PAST) load(t + AHEAD, dst, 2 * S + (K != 1));
-        else ld.issue(k0, kdim - k0, dst, gw, 2 * S + (K != 1));
-        MHG_ORDER();
-      }
-      reads_from<S, K + 1, PAST>(slot, t);
+      reads_from<S, K + 1>(slot);
     }
   }
   // Every load of slab t this wave makes (prologue).
@@ -329,16 +316,33 @@ struct W8Gemm {
                                              in ? uint32_t((int64_t(r) * p.ldc + 8 * c) * 2) : kOut, 0, 0, 0);
   }
 
-  // Memory phase for slab t: read all of the wave's fragments of slab t and request
-  // loads of slab t+4 (into the slot of slab t-1, which every wave has finished
-  // reading: the last reader ended its phase with every read complete).
-  template <int S, bool PAST>
-  __device__ __forceinline__ void mem_steps(uint32_t slot, int t) {
-    if constexpr (S < STEPS) { reads_from<S, 0, PAST>(slot, t); mem_steps<S + 1, PAST>(slot, t); }
+  // Memory phase for slab t: read all of the wave's fragments of slab t, then request
+  // its loads of slab t+4 (into the slot of slab t-1, which every wave has finished
+  // reading: the last reader ended its phase with every read complete).  The requests
+  // come after the reads: issued among them they kept the reads apart (about 20 cycles
+  // each); after them they overlap the wait for the last reads (4096^3: 1250 -> 1280
+  // TFLOP/s).  PAST: slab t + 4 lies past K (the last four slabs of the 256 x 256 loop).
+  template <int S>
+  __device__ __forceinline__ void mem_steps(uint32_t slot) {
+    if constexpr (S < STEPS) { reads_from<S, 0>(slot); mem_steps<S + 1>(slot); }
   }
   template <bool PAST = false>
   __device__ __forceinline__ void mem(int t) {
-    mem_steps<0, PAST>(slot_addr(t), t);
+    mem_steps<0>(slot_addr(t));
+    const int k0 = (t + AHEAD) * BK;
+    const uint32_t dst = slot_addr(t + AHEAD);
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      if constexpr (ALT) {
+        ld.issue(k0, kdim - k0, dst, gw, j);
+        ld2.issue(k0, kdim - k0, dst, gw, j);
+      } else if constexpr (PAST) {
+        load(t + AHEAD, dst, j);
+      } else {
+        ld.issue(k0, kdim - k0, dst, gw, j);
+      }
+      MHG_ORDER();
+    }
     wait_lgkm<0>();
     MHG_ORDER();
   }
