@@ -9,7 +9,10 @@
 //     end;
 //   * 64 x 64, 128-deep slabs: as 128 x 128, with 32 x 32 of C per wave.
 // Every slab is 32 KiB (16 KiB of A at +0, 16 KiB of B at +16 KiB), so all shapes use
-// the same ring: five slots, 160 KB, four slabs requested ahead.
+// the same ring: five slots, 160 KB, four slabs requested ahead.  One exception: the
+// 256 x 256 tile with both operands K-contiguous (row-major A, column-major B) keeps A
+// in a ring of slab pairs (whole 128-byte rows; a single 32-deep slab would request
+// half lines) beside a ring of B slabs.
 //
 // The three tiling levels of "Tiling 策略与内存层次优化" (multi-level tiling) sized for
 // gfx950:
@@ -70,9 +73,11 @@ constexpr uint32_t kOut = 0x80000000u;          // beyond every buffer range: lo
 
 // The tile shapes.  FM x FN accumulators of 32 x 32 per wave; KSPLIT = 2: the groups
 // take alternate slabs (halves of K) instead of halves of the rows.
-struct Tile256 { static constexpr int BM = 256, BN = 256, BK = 32, FM = 4, FN = 2, KSPLIT = 1; };
-struct Tile128 { static constexpr int BM = 128, BN = 128, BK = 64, FM = 2, FN = 2, KSPLIT = 2; };
-struct Tile64 { static constexpr int BM = 64, BN = 64, BK = 128, FM = 1, FN = 1, KSPLIT = 2; };
+// PAIRA: with A row-major and B column-major, the 256 x 256 tile brings A in pairs of
+// slabs, whole 128-byte rows (see the pair ring below).
+struct Tile256 { static constexpr int BM = 256, BN = 256, BK = 32, FM = 4, FN = 2, KSPLIT = 1; static constexpr bool PAIRA = true; };
+struct Tile128 { static constexpr int BM = 128, BN = 128, BK = 64, FM = 2, FN = 2, KSPLIT = 2; static constexpr bool PAIRA = false; };
+struct Tile64 { static constexpr int BM = 64, BN = 64, BK = 128, FM = 1, FN = 1, KSPLIT = 2; static constexpr bool PAIRA = false; };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, 0x7fffffff, 0x00020000);
@@ -158,6 +163,36 @@ struct Loader {
   }
 };
 
+// A row-major A in pairs of slabs (PAIRA): the tile's 256 rows of 2 BK = 64 values, 128
+// bytes, in two 16 KiB halves of 128 rows; load j of wave w in half h brings rows
+// 128 h + 32 j + 8 w .. + 7, lane l the chunk (l % 8) ^ kswz(row) of row 128 h + 32 j +
+// 8 w + l / 8.  The swizzle of a row depends on its bits 1..3 only, so a lane's chunk is
+// the same for every load and both halves, and a load's offset is the lane's base plus
+// a wave-uniform multiple of the leading dimension.
+struct PairLoader {
+  uint32_t base;             // lane's byte offset at row 8 w + l / 8, its chunk
+  int rows_left;             // M - (tile row of that lane's first row)
+  int kc;                    // k of the lane's chunk within the pair (8 c)
+  const uint16_t *origin0;   // A at the tile's first row, k = 0 (wave-uniform)
+  int64_t ld2;               // 2 * lda (bytes per row, wave-uniform)
+  __device__ __forceinline__ void init(const uint16_t *g, int64_t ld, int m0, int64_t M, int wave, int lane) {
+    const int r0 = 8 * wave + (lane >> 3), c = (lane & 7) ^ kswz<64>(r0);
+    base = uint32_t((int64_t(r0) * ld + 8 * c) * 2);
+    rows_left = int(M - m0 < (int64_t(1) << 30) ? M - m0 : (int64_t(1) << 30)) - r0;
+    kc = 8 * c;
+    origin0 = reinterpret_cast<const uint16_t *>(first_lane_u64(reinterpret_cast<uint64_t>(g + int64_t(m0) * ld)));
+    ld2 = int64_t(first_lane_u64(uint64_t(2 * ld)));
+  }
+  __device__ __forceinline__ void issue(int k0, int k_left, uint32_t dst, uint32_t wave, int j, int h) const {
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(origin0 + k0);
+    const int row = 128 * h + 32 * j;
+    const bool in = row < rows_left && kc < k_left;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (MHG_LDS void *)(size_t)(dst + uint32_t(h) * 16384u + (GROUP * j + wave) * 1024), 16,
+        in ? base + uint32_t(int64_t(row) * ld2) : kOut, 0, 0, 0);
+  }
+};
+
 // Fragment addressing.  A 32 x 16 fragment (32 rows of m or n, 16 k) for
 // v_mfma_f32_32x32x16: lane l holds row l % 32, k = 8 (l / 32) .. +7 of the 16-deep
 // step s.
@@ -219,6 +254,16 @@ struct W8Gemm {
   static constexpr int WTM = 32 * FM, WTN = 32 * FN;      // a wave's block of C
   static_assert(BM * BK * 2 == OP_BYTES && BN * BK * 2 == OP_BYTES, "slab size");
   static_assert(!PRIOR || (!ALT && FM == 4 && FN == 2), "prior C through LDS: 256 x 256 tile only");
+  // PA: A (row-major) in a ring of three 32 KiB pair slots, each the tile's 256 rows of
+  // 2 BK values (128 bytes) of two consecutive slabs; B in a ring of four 16 KiB slots.
+  // A 32-deep slab holds only 64 bytes of a K-contiguous row, so its loads are half-line
+  // requests; in pairs they are whole lines.  Used when B is K-contiguous as well
+  // (column-major), where it measured 1157 -> 1207 TFLOP/s at 4096^3 bf16; with B
+  // row-major the shallower B ring (three slabs ahead instead of four) cost more than
+  // the whole lines gained (1260 -> 1230).
+  static constexpr bool PA = TL::PAIRA && !ALT && A_KC && B_KC && !PRIOR;
+  static constexpr int BKA = PA ? 2 * BK : BK;            // k values in an LDS row of A
+  static constexpr uint32_t PA_B = 3 * 32768;              // byte offset of the B ring
 
   const LaunchArgs &p;
   int m0, n0;
@@ -229,6 +274,8 @@ struct W8Gemm {
   // 256 x 256: ld is the group's operand (group 0 A, group 1 B); 128 x 128: ld is A and
   // ld2 B of the group's own slabs.
   Loader ld, ld2;
+  PairLoader lp;              // PA: group 0's loader of A
+  uint32_t fa_cur;            // fa_off[0] with the slab's half of an A pair applied (PA)
   // Lane offsets of the fragment reads within an operand slab (step 0), the wave's
   // block offset included: K-contiguous operands use [0] (step s is [0] ^ 32 s, block i
   // adds 64 BK i); M/N-contiguous ones one per block (step s adds 16 s k-rows).
@@ -254,13 +301,13 @@ struct W8Gemm {
   }
   // Read k of the wave's step S (0 or 1) from the slab whose A area is `slot`.
   template <int S, int K>
-  __device__ __forceinline__ void read(uint32_t slot) {
+  __device__ __forceinline__ void read(uint32_t sa, uint32_t slot) {
     constexpr int f = read_frag(K), h = read_half(K);
     if constexpr (f < FM) {
       if constexpr (A_KC) {
-        ds_b128<64 * BK * f>(*reinterpret_cast<u32x4 *>(&fa[S][f][0]), slot + (fa_off[0] ^ uint32_t(32 * S)));
+        ds_b128<64 * BKA * f>(*reinterpret_cast<u32x4 *>(&fa[S][f][0]), sa + (fa_cur ^ uint32_t(32 * S)));
       } else {
-        ds_tr<16 * S * 2 * BM + 4 * 2 * BM * h>(fa[S][f][h], slot + fa_off[f]);
+        ds_tr<16 * S * 2 * BM + 4 * 2 * BM * h>(fa[S][f][h], sa + fa_off[f]);
       }
     } else {
       constexpr int j = f - FM;
@@ -273,10 +320,10 @@ struct W8Gemm {
   }
   // Reads K .. T-1 of step S, back to back.
   template <int S, int K>
-  __device__ __forceinline__ void reads_from(uint32_t slot) {
+  __device__ __forceinline__ void reads_from(uint32_t sa, uint32_t slot) {
     if constexpr (K < T) {
-      read<S, K>(slot); MHG_ORDER();
-      reads_from<S, K + 1>(slot);
+      read<S, K>(sa, slot); MHG_ORDER();
+      reads_from<S, K + 1>(sa, slot);
     }
   }
   // Every load of slab t this wave makes (prologue).
@@ -323,12 +370,33 @@ struct W8Gemm {
   // each); after them they overlap the wait for the last reads (4096^3: 1250 -> 1280
   // TFLOP/s).  PAST: slab t + 4 lies past K (the last four slabs of the 256 x 256 loop).
   template <int S>
-  __device__ __forceinline__ void mem_steps(uint32_t slot) {
-    if constexpr (S < STEPS) { reads_from<S, 0>(slot); mem_steps<S + 1>(slot); }
+  __device__ __forceinline__ void mem_steps(uint32_t sa, uint32_t slot) {
+    if constexpr (S < STEPS) { reads_from<S, 0>(sa, slot); mem_steps<S + 1>(sa, slot); }
+  }
+  // PA memory phase for slab t: reads from A's pair slot (t / 2) % 3 (half t % 2 of its
+  // rows) and B's slot t % 4, then group 0 requests half t % 2 of A's pair (t + 4) / 2
+  // and group 1 B of slab t + 3.
+  __device__ __forceinline__ void mem_pa(int t) {
+    fa_cur = fa_off[0] ^ uint32_t(64 * (t & 1));
+    mem_steps<0>(lds0 + uint32_t((t >> 1) % 3) * 32768u, lds0 + PA_B + uint32_t(t & 3) * 16384u - OP_BYTES);
+    if (grp == 0) {
+      const int pr = (t + 4) >> 1, k0 = pr * 2 * BK;
+      const uint32_t dst = lds0 + uint32_t(pr % 3) * 32768u;
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) { lp.issue(k0, kdim - k0, dst, gw, j, t & 1); MHG_ORDER(); }
+    } else {
+      const int k0 = (t + 3) * BK;
+      const uint32_t dst = lds0 + PA_B + uint32_t((t + 3) & 3) * 16384u - OP_BYTES;
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) { ld.issue(k0, kdim - k0, dst, gw, j); MHG_ORDER(); }
+    }
+    wait_lgkm<0>();
+    MHG_ORDER();
   }
   template <bool PAST = false>
   __device__ __forceinline__ void mem(int t) {
-    mem_steps<0>(slot_addr(t));
+    fa_cur = fa_off[0];
+    mem_steps<0>(slot_addr(t), slot_addr(t));
     const int k0 = (t + AHEAD) * BK;
     const uint32_t dst = slot_addr(t + AHEAD);
 #pragma unroll
@@ -376,8 +444,17 @@ struct W8Gemm {
     if (!ALT) {              // groups split the rows (128 x 64 blocks) and the operands
       wm = int(grp);
       wn = int(gw);
-      if (grp == 0) ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
-      else ld.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
+      if constexpr (PA) {    // group 0: rows 0..127 (ld) and 128..255 (ld2) of A's pairs
+        if (grp == 0) {
+          lp.init(A, p.lda, m0, p.M, int(gw), lane);
+        } else {
+          ld.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
+        }
+      } else if (grp == 0) {
+        ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
+      } else {
+        ld.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
+      }
     } else {                 // groups take alternate slabs; WTM x WTN blocks, 2 x 2 of them
       wm = int(gw >> 1);
       wn = int(gw & 1);
@@ -385,7 +462,7 @@ struct W8Gemm {
       ld2.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
     }
     if (A_KC) {
-      fa_off[0] = kc_lane<BK>(lane) + 64 * BK * FM * wm;
+      fa_off[0] = kc_lane<BKA>(lane) + 64 * BKA * FM * wm;
     } else {
 #pragma unroll
       for (int i = 0; i < FM; ++i) fa_off[i] = mn_lane<BM>(lane, FM * wm + i);
@@ -408,7 +485,42 @@ struct W8Gemm {
     // phase behind and the two groups of a SIMD alternate between reading and
     // multiplying.
     wait_lgkm<0>();                     // nothing else counts against lgkmcnt below
-    if (!ALT) {
+    if constexpr (PA) {
+      // Prologue: group 0 requests A's pairs 0 and 1 (slabs 0..3), group 1 B of slabs
+      // 0..2.  Group 0 needs pair t / 2 whole before slab t is read: its second half was
+      // requested two memory phases earlier, so after multiplying at most 8 loads may
+      // be in flight.  Group 1 needs B of slab t after its memory phase of slab t - 1:
+      // requested three phases earlier, at most 8 in flight.
+      if (grp == 0) {
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < LOADS; ++j)
+              lp.issue(pr * 2 * BK, kdim - pr * 2 * BK, lds0 + uint32_t(pr) * 32768u, gw, j, h);
+      } else {
+#pragma unroll
+        for (int u = 0; u < 3; ++u)
+#pragma unroll
+          for (int j = 0; j < LOADS; ++j)
+            ld.issue(u * BK, kdim - u * BK, lds0 + PA_B + uint32_t(u) * 16384u - OP_BYTES, gw, j);
+      }
+      wait_vm<2 * LOADS>();
+      barrier();
+      if (grp == 1) barrier();
+      MHG_ORDER();
+      for (int t = 0; t < KT; ++t) {
+        mem_pa(t);
+        if (grp == 1) wait_vm<2 * LOADS>(); else wait_vm<3 * LOADS>();
+        barrier();
+        MHG_ORDER();
+        compute();
+        if (grp == 0) wait_vm<2 * LOADS>(); else wait_vm<3 * LOADS>();
+        barrier();
+        MHG_ORDER();
+      }
+    } else if (!ALT) {
       // Both groups read every slab: in phase 2t group 0 reads slab t while group 1
       // multiplies slab t-1, in phase 2t+1 group 0 multiplies slab t while group 1 reads
       // it.  Group 0 requests A of slab t+4 in phase 2t, group 1 B of slab t+4 in phase
