@@ -258,9 +258,9 @@ struct W8Gemm {
   // 2 BK values (128 bytes) of two consecutive slabs; B in a ring of four 16 KiB slots.
   // A 32-deep slab holds only 64 bytes of a K-contiguous row, so its loads are half-line
   // requests; in pairs they are whole lines.  Used when B is K-contiguous as well
-  // (column-major), where it measured 1157 -> 1207 TFLOP/s at 4096^3 bf16; with B
-  // row-major the shallower B ring (three slabs ahead instead of four) cost more than
-  // the whole lines gained (1260 -> 1230).
+  // (column-major), where it measured 1157 -> 1207 TFLOP/s at 4096^3 bf16 (about 2%
+  // more with B four slabs ahead, its slot refilled right after group 1's reads); with
+  // B row-major it was slower either way (1317 -> 1256 with B four ahead).
   static constexpr bool PA = TL::PAIRA && !ALT && A_KC && B_KC && !PRIOR;
   static constexpr int BKA = PA ? 2 * BK : BK;            // k values in an LDS row of A
   static constexpr uint32_t PA_B = 3 * 32768;              // byte offset of the B ring
@@ -373,9 +373,10 @@ struct W8Gemm {
   __device__ __forceinline__ void mem_steps(uint32_t sa, uint32_t slot) {
     if constexpr (S < STEPS) { reads_from<S, 0>(sa, slot); mem_steps<S + 1>(sa, slot); }
   }
-  // PA memory phase for slab t: reads from A's pair slot (t / 2) % 3 (half t % 2 of its
-  // rows) and B's slot t % 4, then group 0 requests half t % 2 of A's pair (t + 4) / 2
-  // and group 1 B of slab t + 3.
+  // PA memory phase for slab t: reads from A's pair slot (t / 2) % 3 (the slab's half of
+  // each row) and B's slot t % 4, then group 0 requests half t % 2 of A's pair
+  // (t + 4) / 2 (rows 128 (t % 2) ..) and group 1, once its reads are complete, B of
+  // slab t + 4 into slab t's B slot: group 1 is the last to read each slab.
   __device__ __forceinline__ void mem_pa(int t) {
     fa_cur = fa_off[0] ^ uint32_t(64 * (t & 1));
     mem_steps<0>(lds0 + uint32_t((t >> 1) % 3) * 32768u, lds0 + PA_B + uint32_t(t & 3) * 16384u - OP_BYTES);
@@ -385,8 +386,10 @@ struct W8Gemm {
 #pragma unroll
       for (int j = 0; j < LOADS; ++j) { lp.issue(k0, kdim - k0, dst, gw, j, t & 1); MHG_ORDER(); }
     } else {
-      const int k0 = (t + 3) * BK;
-      const uint32_t dst = lds0 + PA_B + uint32_t((t + 3) & 3) * 16384u - OP_BYTES;
+      wait_lgkm<0>();       // this group reads slab t last: its B slot takes slab t + 4
+      MHG_ORDER();
+      const int k0 = (t + 4) * BK;
+      const uint32_t dst = lds0 + PA_B + uint32_t(t & 3) * 16384u - OP_BYTES;
 #pragma unroll
       for (int j = 0; j < LOADS; ++j) { ld.issue(k0, kdim - k0, dst, gw, j); MHG_ORDER(); }
     }
@@ -487,10 +490,10 @@ struct W8Gemm {
     wait_lgkm<0>();                     // nothing else counts against lgkmcnt below
     if constexpr (PA) {
       // Prologue: group 0 requests A's pairs 0 and 1 (slabs 0..3), group 1 B of slabs
-      // 0..2.  Group 0 needs pair t / 2 whole before slab t is read: its second half was
+      // 0..3.  Group 0 needs pair t / 2 whole before slab t is read: its second half was
       // requested two memory phases earlier, so after multiplying at most 8 loads may
       // be in flight.  Group 1 needs B of slab t after its memory phase of slab t - 1:
-      // requested three phases earlier, at most 8 in flight.
+      // requested four memory phases earlier, at most 12 in flight.
       if (grp == 0) {
 #pragma unroll
         for (int pr = 0; pr < 2; ++pr)
@@ -501,18 +504,18 @@ struct W8Gemm {
               lp.issue(pr * 2 * BK, kdim - pr * 2 * BK, lds0 + uint32_t(pr) * 32768u, gw, j, h);
       } else {
 #pragma unroll
-        for (int u = 0; u < 3; ++u)
+        for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int j = 0; j < LOADS; ++j)
             ld.issue(u * BK, kdim - u * BK, lds0 + PA_B + uint32_t(u) * 16384u - OP_BYTES, gw, j);
       }
-      wait_vm<2 * LOADS>();
+      if (grp == 1) wait_vm<3 * LOADS>(); else wait_vm<2 * LOADS>();
       barrier();
       if (grp == 1) barrier();
       MHG_ORDER();
       for (int t = 0; t < KT; ++t) {
         mem_pa(t);
-        if (grp == 1) wait_vm<2 * LOADS>(); else wait_vm<3 * LOADS>();
+        wait_vm<3 * LOADS>();
         barrier();
         MHG_ORDER();
         compute();
