@@ -2,8 +2,9 @@
 """Benchmark of the tiled GEMM on one MI355X.
 
 One step = one call of the planned product (gemm_run) on one batch of synthetic
-operands already resident in HBM.  The headline workload is the bf16 4096^3 product
-(bf16 output, fp32 accumulation): value = 2*M*N*K / (wall seconds per step), in
+operands already resident in HBM.  Before the warm-up steps, the headline plan runs
+SETTLE_CALLS untimed calls so that the clock has settled under the sustained load.
+The headline workload is the bf16 4096^3 product (bf16 output, fp32 accumulation): value = 2*M*N*K / (wall seconds per step), in
 TFLOP/s.  The other measured shapes are reported under "per_shape" with their
 roofline fraction: min(peak, intensity * 8 TB/s), where intensity counts each
 operand once (2MNK over the bytes of A, B and C).
@@ -37,6 +38,13 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 HBM_GBPS = 8000.0
 ELEM = {"f32": 4, "f16": 2, "bf16": 2}
 ROTATE_BYTES = 512 << 20       # working set of rotated operand copies, > 256 MB cache
+# Untimed calls of the headline plan before its warm-up.  Under a sustained 4096^3 load
+# the power manager takes the clock down over the first ~150 calls (about 130 us a call
+# instead of 105-115); these calls (~0.2 s) let it settle, so that the warm-up and the
+# timed steps see the steady state whatever --warmup the caller passes.
+SETTLE_CALLS = 2000
+# Window of the clock probe: 2,000,000 ticks of the 100 MHz real-time counter (20 ms).
+CLOCK_TICKS = 2_000_000
 
 
 def log(*a):
@@ -68,10 +76,32 @@ def roofline_of(w):
     return ai, roof, bound
 
 
-def measure(name, steps, warmup, per_call=False, epilogue=False):
-    """Time `steps` calls after `warmup` untimed calls.  Returns a dict of figures.
-    epilogue: run through the fused epilogue with alpha = beta = 1, a bias and ReLU
-    (C is read as well as written; its bytes and the bias's count in the GB/s)."""
+def clock_during(run, first):
+    """Shader clock (MHz) while the calls of `run` stream: the one-wave clock probe runs
+    on a second stream (default priority) for CLOCK_TICKS real-time ticks, started after
+    100 calls are queued and followed by enough calls to outlast its window."""
+    import torch
+
+    import memory_hierarchy_optimisation_amd as mh
+
+    side = torch.cuda.Stream()
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(100):
+        run(first + i)
+    mh.gemm_clock_probe(out.data_ptr(), CLOCK_TICKS, stream=side.cuda_stream)
+    for i in range(100, 600):
+        run(first + i)
+    torch.cuda.synchronize()
+    cycles, ticks = (int(v) for v in out.cpu().tolist())
+    return 100.0 * cycles / ticks
+
+
+def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock=False):
+    """Time `steps` calls after `settle` + `warmup` untimed calls.  Returns a dict of
+    figures.  epilogue: run through the fused epilogue with alpha = beta = 1, a bias and
+    ReLU (C is read as well as written; its bytes and the bias's count in the GB/s).
+    clock: afterwards, read the shader clock during a further run of calls."""
     import torch
 
     import memory_hierarchy_optimisation_amd as mh
@@ -106,7 +136,7 @@ def measure(name, steps, warmup, per_call=False, epilogue=False):
             mh.gemm_run(plan, a_ptr[i % copies], b_ptr[i % copies], c_ptr, handle)
 
     try:
-        for i in range(warmup):
+        for i in range(settle + warmup):
             run(i)
         torch.cuda.synchronize()
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -128,6 +158,7 @@ def measure(name, steps, warmup, per_call=False, epilogue=False):
                 b.record(stream)
             torch.cuda.synchronize()
             calls = sorted(a.elapsed_time(b) for a, b in evs)
+        clock_mhz = clock_during(run, steps) if clock else None
     finally:
         mh.gemm_destroy(plan)
     flops, nbytes = algorithmic(w)
@@ -140,6 +171,7 @@ def measure(name, steps, warmup, per_call=False, epilogue=False):
         "layout": ("A col" if w.a_col else "A row") + (", B col" if w.b_col else ", B row"),
         "tile": f"{desc['bm']}x{desc['bn']}x{desc['bk']}", "kind": desc["kind"],
         "grid": desc["grid_x"] * desc["grid_y"] * desc["grid_z"], "rotated_copies": copies,
+        "settle_calls": settle, "warmup_calls": warmup, "timed_calls": steps,
         "ms_per_step": ms_step, "kernel_ms_event": event_ms,
         "tflops": flops / (ms_step / 1000.0) / 1e12,
         "kernel_tflops": flops / (event_ms / 1000.0) / 1e12,
@@ -150,6 +182,8 @@ def measure(name, steps, warmup, per_call=False, epilogue=False):
     if calls:
         k = len(calls)
         out["kernel_ms_p10_p50_p90"] = [calls[k // 10], calls[k // 2], calls[(9 * k) // 10]]
+    if clock_mhz is not None:
+        out["clock_mhz"] = clock_mhz
     return out
 
 
@@ -319,11 +353,56 @@ def summarize_traffic(fetch_csv, write_csv, name, digest, out_path):
     log("\n".join(lines))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_threads():
+    """Cores the oracle may use: the CPUs this process is allowed to run on, capped by
+    OMP_NUM_THREADS when the environment sets it (the host's share for one GPU)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return n
+
+
+def oracle_timings(names, threads):
+    """Whole products of the small workloads through the oracle, compute loop only."""
+    import oracle
+    import synth
+
+    out = []
+    for name in names:
+        w = synth.WORKLOADS[name]
+        As, lda, Bs, ldb, _, _ = synth.workload_operands(w)
+        a = synth.to_storage_numpy(As)
+        b = synth.to_storage_numpy(Bs)
+        for n in threads:
+            oracle.set_threads(n)
+            t0 = time.perf_counter()
+            oracle.gemm(w.M, w.N, w.K, a, lda, b, ldb, w.dtype, a_col=w.a_col, b_col=w.b_col)
+            t = time.perf_counter() - t0
+            out.append({"workload": name, "threads": n, "seconds": round(t, 4),
+                        "gflops": round(2.0 * w.M * w.N * w.K / t / 1e9, 3)})
+            log(f"[bench] oracle {name} on {n} thread(s): {t:.3f} s")
+    return out
+
+
 def cpu_baseline(name, seconds):
     """The oracle as it stands, on the host cores, over the first rows of the product."""
     import oracle
     import synth
 
+    threads = host_threads()
+    oracle.set_threads(threads)
     w = synth.WORKLOADS[name]
     As, lda, Bs, ldb, _, _ = synth.workload_operands(w)
     a = synth.to_storage_numpy(As)
@@ -337,11 +416,17 @@ def cpu_baseline(name, seconds):
     oracle.gemm(w.M, w.N, w.K, a, lda, b, ldb, w.dtype, a_col=w.a_col, b_col=w.b_col, rows=(0, rows))
     t = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
-    return {
+    res = {
         "value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.max_threads(), "kind": "oracle",
         "sample": f"rows 0..{rows - 1} of the {w.M}x{w.N}x{w.K} {w.dtype} product "
                   f"({rows * w.N} of {w.M * w.N} outputs, {t:.1f} s, binary64 triple loop)",
+        "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0)),
     }
+    # The three small workloads in full, on all the cores and on one.
+    res["small_workloads"] = oracle_timings(["f32_64", "f16_1024", "f16_1000", "f16_2048_nt"],
+                                            sorted({threads, 1}, reverse=True))
+    oracle.set_threads(threads)
+    return res
 
 
 def main():
@@ -377,9 +462,11 @@ def main():
     torch.cuda.set_device(0)
     log(f"[bench] device {torch.cuda.get_device_name(0)}; headline {args.workload}")
 
-    head = measure(args.workload, args.steps, args.warmup, per_call=True)
+    head = measure(args.workload, args.steps, args.warmup, settle=SETTLE_CALLS, per_call=True, clock=True)
     log(f"[bench] headline {head['workload']}: {head['tflops']:.1f} TFLOP/s "
-        f"({head['ms_per_step'] * 1000:.1f} us/step, kernel {head['kernel_ms_event'] * 1000:.1f} us)")
+        f"({head['ms_per_step'] * 1000:.1f} us/step, kernel {head['kernel_ms_event'] * 1000:.1f} us, "
+        f"per call p10/p50/p90 {[round(1000 * v, 1) for v in head.get('kernel_ms_p10_p50_p90', [])]} us, "
+        f"clock {head['clock_mhz']:.0f} MHz)")
     shapes = []
     if not args.no_per_shape:
         for name in PER_SHAPE:
@@ -391,9 +478,9 @@ def main():
                 f"{100 * r['frac_of_roofline']:.1f}% of the {r['bound']} roofline, tile {r['tile']}")
     extras = {}
     if not args.no_per_shape and not args.no_extras:
-        # The same warm-up as the headline: the clock settles again after the smaller
-        # per-shape lines, and the timed calls should see the steady state.
-        r = measure(args.workload, 100, args.warmup, per_call=True, epilogue=True)
+        # The same settling as the headline and the per-shape lines' fixed warm-up: the
+        # clock settles again after the smaller per-shape lines.
+        r = measure(args.workload, 100, 300, settle=SETTLE_CALLS, per_call=True, epilogue=True, clock=True)
         extras["epilogue"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         log(f"[bench] {r['workload']} (alpha, beta = 1, bias, ReLU): {r['kernel_tflops']:.1f} TFLOP/s, "
             f"kernel {r['kernel_ms_event'] * 1000:.1f} us against {head['kernel_ms_event'] * 1000:.1f} us plain")
@@ -424,6 +511,11 @@ def main():
         "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "cpu_baseline": cpu,
+        "clock_mhz": round(head["clock_mhz"], 1),
+        "clock_note": "average shader clock over 20 ms of further headline calls (s_memtime over "
+                      "s_memrealtime on a one-wave probe on a second stream)",
+        "kernel_ms_p10_p50_p90": head.get("kernel_ms_p10_p50_p90"),
+        "settle_calls": SETTLE_CALLS,
         "kernel_source_digest": kernel_source_digest(),
         "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                       for r in shapes],

@@ -191,6 +191,19 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C,
 int gemm_transpose(const void *in, void *out, int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
                    int32_t elem_bytes, void *stream);
 
+/*
+ * gemm_clock_probe -- a measurement helper beside the product (the pages' profiling
+ * advice asks for the conditions a kernel ran under, and the clock of this part
+ * moves with its load).  Launches one wave on `stream` that waits `ticks` periods of
+ * the constant 100 MHz real-time counter and writes out[0] = shader-clock cycles and
+ * out[1] = real-time ticks (>= ticks) elapsed over that window; the average shader
+ * clock in MHz is 100 * out[0] / out[1].  Run on a second stream while GEMM calls run
+ * on another, it reads the clock they run at.  out: device pointer to two uint64,
+ * 8-byte aligned; 1 <= ticks <= 1e9 (ten seconds).  Asynchronous.  Returns GEMM_OK,
+ * GEMM_ERR_INVALID_ARG or GEMM_ERR_HIP.
+ */
+int gemm_clock_probe(uint64_t *out, int64_t ticks, void *stream);
+
 /* gemm_destroy -- release a plan and its workspace.  NULL is ignored. */
 void gemm_destroy(gemm_plan_t plan);
 

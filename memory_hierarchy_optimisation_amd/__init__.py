@@ -40,7 +40,7 @@ DESCRIBE_FIELDS = ("kind", "bm", "bn", "bk", "waves_m", "waves_n", "stages", "sp
 
 EXPORTS = ("gemm_plan", "gemm_plan_config", "gemm_run", "gemm_run_epilogue", "gemm_destroy",
            "gemm_last_error", "gemm_plan_describe", "gemm_catalogue", "gemm_autotune", "gemm_tune_save",
-           "gemm_tune_load", "gemm_tune_clear", "gemm_transpose")
+           "gemm_tune_load", "gemm_tune_clear", "gemm_transpose", "gemm_clock_probe")
 
 
 class Epilogue(ctypes.Structure):
@@ -103,6 +103,8 @@ def _load():
     lib.gemm_tune_clear.restype = None
     lib.gemm_transpose.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp]
     lib.gemm_transpose.restype = i32
+    lib.gemm_clock_probe.argtypes = [vp, i64, vp]
+    lib.gemm_clock_probe.restype = i32
     runtimes = hip_runtimes_mapped()
     if len(runtimes) > 1:
         raise ImportError("more than one HIP runtime is mapped into this process "
@@ -233,3 +235,10 @@ def gemm_transpose(inp, out, rows, cols, ld_in, ld_out, elem_bytes, stream=None)
     if rc != GEMM_OK:
         raise GemmError(rc, gemm_last_error())
 
+
+def gemm_clock_probe(out, ticks, stream=None):
+    """Enqueue the one-wave clock probe: out (device, two uint64) receives the shader
+    cycles and the 100 MHz real-time ticks of a window of `ticks` ticks."""
+    rc = _lib.gemm_clock_probe(_ptr(out), int(ticks), _stream(stream))
+    if rc != GEMM_OK:
+        raise GemmError(rc, gemm_last_error())

@@ -18,15 +18,13 @@ namespace mhg {
 hipError_t launch_fma(int launcher, const LaunchArgs &p, hipStream_t s);
 hipError_t launch_mfma(int launcher, const LaunchArgs &p, hipStream_t s);
 hipError_t launch_fill(const LaunchArgs &p, hipStream_t s);
-hipError_t launch_ring(int launcher, const LaunchArgs &p, hipStream_t s);
-bool ring_supported(const LaunchArgs &p, int bm, int bn);
-hipError_t launch_big(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_w8(const LaunchArgs &p, int bm, hipStream_t s);
 hipError_t launch_skinny(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_mfma32(const LaunchArgs &p, hipStream_t s);
 hipError_t launch_zero_words(void *w, int64_t n, hipStream_t s);
 hipError_t launch_transpose(const void *in, void *out, int64_t rows, int64_t cols, int64_t ld_in, int64_t ld_out,
                             int elem_bytes, hipStream_t s);
+hipError_t launch_clock_probe(uint64_t *out, uint64_t ticks, hipStream_t s);
 }  // namespace mhg
 
 struct gemm_plan_s {
@@ -236,8 +234,9 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
     int count;
     const mhg::Variant *cat = mhg::catalogue(&count);
     const mhg::Variant *v = &cat[d.variant];
-    const bool direct_ok = v->launcher == mhg::L_SKINNY ? (a.vec_a && a.vec_b)
-                                                        : mhg::ring_supported(a, v->cfg.bm, v->cfg.bn);
+    // Direct 16-byte staging: the plan checked extents, leading dimensions and slab
+    // spans; what it cannot see is the alignment of the pointers.
+    const bool direct_ok = a.vec_a && a.vec_b;
     if (v->fallback >= 0 && !direct_ok) {
       v = mhg::variant_of_launcher(v->fallback);   // register-staged: any alignment
       a.gm = int((d.M + v->cfg.bm - 1) / v->cfg.bm);
@@ -257,10 +256,6 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
     switch (v->launcher) {
       case mhg::L_FMA_32: case mhg::L_FMA_64: case mhg::L_FMA_128:
         e = mhg::launch_fma(v->launcher, a, s); break;
-      case mhg::L_RING_256x256_W4: case mhg::L_RING_256x256_W8: case mhg::L_RING_128x128_W4:
-        e = mhg::launch_ring(v->launcher, a, s); break;
-      case mhg::L_BIG_256:
-        e = mhg::launch_big(a, s); break;
       case mhg::L_W8_256: case mhg::L_W8_128: case mhg::L_W8_64:
         e = mhg::launch_w8(a, v->cfg.bm, s); break;
       case mhg::L_SKINNY:
@@ -317,6 +312,24 @@ int gemm_transpose(const void *in, void *out, int64_t rows, int64_t cols, int64_
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     set_error(std::string("gemm_transpose: launch failed: ") + hipGetErrorString(e));
+    return GEMM_ERR_HIP;
+  }
+  set_error("");
+  return GEMM_OK;
+}
+
+int gemm_clock_probe(uint64_t *out, int64_t ticks, void *stream) {
+  if (!out || reinterpret_cast<uintptr_t>(out) % 8 != 0) {
+    set_error("gemm_clock_probe: NULL or misaligned output");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  if (ticks < 1 || ticks > 1000000000) {
+    set_error("gemm_clock_probe: ticks must lie in [1, 1e9]");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  const hipError_t e = mhg::launch_clock_probe(out, uint64_t(ticks), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    set_error(std::string("gemm_clock_probe: launch failed: ") + hipGetErrorString(e));
     return GEMM_ERR_HIP;
   }
   set_error("");

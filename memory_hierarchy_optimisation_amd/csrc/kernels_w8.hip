@@ -115,9 +115,11 @@ __device__ __forceinline__ uint64_t first_lane_u64(uint64_t v) {
 }
 
 // The slab loads of one wave for one operand.  The four waves of a group fill an
-// operand's 16 KiB slab: load j of group wave w
-// fills LDS bytes (4 j + w) * 1024 .. +1023 of it; lane l writes chunk slot
-// (4 j + w) * 64 + l and loads the chunk that belongs there.
+// operand's 16 KiB slab: load j of group wave w fills LDS bytes b * 1024 .. +1023 of
+// it, b = 4 j + w (loads of one index side by side) or, with OWN, b = 4 w + j (a
+// wave's four loads side by side: at 256 x 256 with a K-contiguous operand that is
+// exactly the 64 rows whose fragments the wave reads); lane l writes chunk slot
+// b * 64 + l and loads the chunk that belongs there.
 struct Loader {
   uint32_t off[LOADS];   // byte offset of the lane's chunk from the slab origin, per load
   int kin[LOADS];        // k of the chunk within the slab; 2^30 when its rows (m or n)
@@ -127,12 +129,14 @@ struct Loader {
   uint32_t lds_off;          // the operand's area in a slot (0: A, OP_BYTES: B)
   // KC: the operand is K-contiguous (rows of m or n with k inside), else M/N-contiguous;
   // R: the tile's extent in m or n.
-  template <bool KC, int R, int BK>
+  template <bool OWN>
+  static __device__ __forceinline__ int block_of(int wave, int j) { return OWN ? GROUP * wave + j : GROUP * j + wave; }
+  template <bool KC, int R, int BK, bool OWN = false>
   __device__ __forceinline__ void init(const uint16_t *g, int64_t ld, int mn0, int64_t MN, int wave, int lane,
                                        uint32_t area) {
 #pragma unroll
     for (int j = 0; j < LOADS; ++j) {
-      const int slot = (GROUP * j + wave) * 64 + lane;
+      const int slot = block_of<OWN>(wave, j) * 64 + lane;
       if (KC) {
         constexpr int CPR = BK / 8;                       // chunks a row
         const int r = slot / CPR, c = (slot % CPR) ^ kswz<BK>(r);
@@ -154,12 +158,15 @@ struct Loader {
     lds_off = area;
   }
   // Load j of the slab at k0 into `slot` (wave-uniform; so is `wave`, the wave's index
-  // in its group: the LDS destination of these loads is a scalar register).
+  // in its group: the LDS destination of these loads is a scalar register).  OWN as
+  // in init.
+  template <bool OWN = false>
   __device__ __forceinline__ void issue(int k0, int k_left, uint32_t slot, uint32_t wave, int j) const {
     const __amdgpu_buffer_rsrc_t rs = rsrc_of(origin0 + k0 * kstep);
     const bool in = kin[j] < k_left;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (MHG_LDS void *)(size_t)(slot + lds_off + (GROUP * j + wave) * 1024),
-                                             16, in ? off[j] : kOut, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rs, (MHG_LDS void *)(size_t)(slot + lds_off + uint32_t(block_of<OWN>(int(wave), j)) * 1024), 16,
+        in ? off[j] : kOut, 0, 0, 0);
   }
 };
 
@@ -375,8 +382,12 @@ struct W8Gemm {
   }
   // PA memory phase for slab t: reads from A's pair slot (t / 2) % 3 (the slab's half of
   // each row) and B's slot t % 4, then group 0 requests half t % 2 of A's pair
-  // (t + 4) / 2 (rows 128 (t % 2) ..) and group 1, once its reads are complete, B of
-  // slab t + 4 into slab t's B slot: group 1 is the last to read each slab.
+  // (t + 4) / 2 (rows 128 (t % 2) ..) and group 1 B of slab t + 4 into slab t's B slot.
+  // B's rows 64 w .. 64 w + 63 of a slab are read by wave w of each group only: by
+  // group 0 one phase earlier (complete before the barrier between), by group 1 now.
+  // So each wave of group 1 refills exactly those rows (OWN loads), once its own reads
+  // are complete; a wave that refilled other rows would overwrite fragments that the
+  // other waves of its group may still be reading in this phase.
   __device__ __forceinline__ void mem_pa(int t) {
     fa_cur = fa_off[0] ^ uint32_t(64 * (t & 1));
     mem_steps<0>(lds0 + uint32_t((t >> 1) % 3) * 32768u, lds0 + PA_B + uint32_t(t & 3) * 16384u - OP_BYTES);
@@ -386,12 +397,12 @@ struct W8Gemm {
 #pragma unroll
       for (int j = 0; j < LOADS; ++j) { lp.issue(k0, kdim - k0, dst, gw, j, t & 1); MHG_ORDER(); }
     } else {
-      wait_lgkm<0>();       // this group reads slab t last: its B slot takes slab t + 4
+      wait_lgkm<0>();       // the wave's own reads of its rows of slab t are complete
       MHG_ORDER();
       const int k0 = (t + 4) * BK;
       const uint32_t dst = lds0 + PA_B + uint32_t(t & 3) * 16384u - OP_BYTES;
 #pragma unroll
-      for (int j = 0; j < LOADS; ++j) { ld.issue(k0, kdim - k0, dst, gw, j); MHG_ORDER(); }
+      for (int j = 0; j < LOADS; ++j) { ld.issue<true>(k0, kdim - k0, dst, gw, j); MHG_ORDER(); }
     }
     wait_lgkm<0>();
     MHG_ORDER();
@@ -451,7 +462,7 @@ struct W8Gemm {
         if (grp == 0) {
           lp.init(A, p.lda, m0, p.M, int(gw), lane);
         } else {
-          ld.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
+          ld.init<B_KC, BN, BK, true>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
         }
       } else if (grp == 0) {
         ld.init<A_KC, BM, BK>(A, p.lda, m0, p.M, gw, lane, 0);
@@ -507,7 +518,7 @@ struct W8Gemm {
         for (int u = 0; u < 4; ++u)
 #pragma unroll
           for (int j = 0; j < LOADS; ++j)
-            ld.issue(u * BK, kdim - u * BK, lds0 + PA_B + uint32_t(u) * 16384u - OP_BYTES, gw, j);
+            ld.issue<true>(u * BK, kdim - u * BK, lds0 + PA_B + uint32_t(u) * 16384u - OP_BYTES, gw, j);
       }
       if (grp == 1) wait_vm<3 * LOADS>(); else wait_vm<2 * LOADS>();
       barrier();

@@ -29,9 +29,10 @@ constexpr unsigned kHalf = (1u << E_F16) | (1u << E_BF16);
 
 // Registers per lane (VGPR + AGPR) each variant needs, from the compiler's
 // resource report of the gfx950 build; used for the occupancy limit.
-// Ring variants come before the register-staged variant of the same tile so that
-// they win ties; `fallback` names the register-staged variant run instead when the
-// operands' alignment rules a ring kernel out at run time (a LauncherId; -1: none).
+// Eight-wave variants come before the register-staged variant of the same tile so
+// that they win ties; `fallback` names the register-staged variant run instead when
+// the operands' alignment rules direct staging out at run time (a LauncherId; -1:
+// none).
 const Variant kCatalogue[] = {
     // kind            bm   bn   bk  wm wn st sk   thr  types  launcher           tm tn fallback
     {{GEMM_KIND_FMA, 32, 32, 32, 4, 1, 2, 1}, 256, kF32, L_FMA_32, 2, 2, -1},
@@ -42,13 +43,9 @@ const Variant kCatalogue[] = {
     {{GEMM_KIND_MFMA, 64, 64, 128, 2, 4, 5, 1}, 512, kHalf, L_W8_64, 2, 2, L_MFMA_64x64},
     {{GEMM_KIND_MFMA, 64, 64, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_64x64, 2, 2, -1},
     {{GEMM_KIND_MFMA, 128, 128, 64, 2, 4, 5, 1}, 512, kHalf, L_W8_128, 4, 4, L_MFMA_128x128},
-    {{GEMM_KIND_MFMA, 128, 128, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_128x128_W4, 4, 4, L_MFMA_128x128},
     {{GEMM_KIND_MFMA, 128, 128, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_128x128, 4, 4, -1},
     {{GEMM_KIND_MFMA, 256, 128, 64, 2, 2, 2, 1}, 256, kHalf, L_MFMA_256x128, 8, 4, -1},
     {{GEMM_KIND_MFMA, 256, 256, 32, 2, 4, 5, 1}, 512, kHalf, L_W8_256, 8, 4, L_MFMA_256x256},
-    {{GEMM_KIND_MFMA, 256, 256, 64, 2, 2, 2, 1}, 256, kHalf, L_BIG_256, 8, 8, L_MFMA_256x256},
-    {{GEMM_KIND_MFMA, 256, 256, 32, 2, 2, 4, 1}, 256, kHalf, L_RING_256x256_W4, 8, 8, L_MFMA_256x256},
-    {{GEMM_KIND_MFMA, 256, 256, 32, 2, 4, 4, 1}, 512, kHalf, L_RING_256x256_W8, 8, 4, L_MFMA_256x256},
     {{GEMM_KIND_MFMA, 256, 256, 64, 2, 4, 2, 1}, 512, kHalf, L_MFMA_256x256, 8, 4, -1},
     // Eight-wave tiles with K split across workgroups: for grids of tiles that leave
     // most compute units idle (fp32 partials added in chunk order by a second kernel).
@@ -66,10 +63,6 @@ const Variant kCatalogue[] = {
     {{GEMM_KIND_SKINNY, 16, 128, 32, 1, 4, 2, 16}, 256, kHalf, L_SKINNY, 1, 8, L_MFMA_64x64},
 };
 
-bool is_ring(int launcher) {
-  return launcher == L_RING_256x256_W4 || launcher == L_RING_256x256_W8 || launcher == L_RING_128x128_W4;
-}
-
 // Largest tile intensity among the catalogue's tiles of an element size; the tile
 // reuse factor is measured against it.
 double best_intensity(int elem, unsigned mask) {
@@ -83,13 +76,9 @@ double best_intensity(int elem, unsigned mask) {
 // registers.  FMA: TM*TN accumulators + TM + TN operands + staged elements.
 // MFMA: 4 fp32 per 16x16 block + fragments + staged 16-byte chunks.
 int regs_estimate(const Variant &v) {
-  if (v.launcher == L_BIG_256) return 512;   // one wave per SIMD: 256 accumulators in AGPRs
   if (v.launcher == L_W8_256 || v.launcher == L_W8_128 || v.launcher == L_W8_64) return 256;   // two waves per SIMD
   if (v.launcher == L_SKINNY) return 128;    // 8 accumulators, two staged rounds, transposes
   if (v.launcher == L_MFMA32_128) return 128;   // 64 accumulators, 32 staged, fragments, addressing
-  if (is_ring(v.launcher)) {   // accumulators + two fragment sets + addressing
-    return v.tm * v.tn * 4 + 2 * (v.tm + v.tn) * 4 + 24;
-  }
   const TileConfig &c = v.cfg;
   if (c.kind == GEMM_KIND_FMA) {
     int staged = (c.bm * c.bk + c.bk * c.bn) / v.threads;
@@ -223,8 +212,7 @@ bool ring_shape_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bo
 }
 
 bool needs_aligned_staging(int launcher) {
-  return is_ring(launcher) || launcher == L_BIG_256 || launcher == L_W8_256 || launcher == L_W8_128 ||
-         launcher == L_W8_64;
+  return launcher == L_W8_256 || launcher == L_W8_128 || launcher == L_W8_64;
 }
 
 bool skinny_shape_ok(const PlanData &p, std::string *why) {
@@ -255,10 +243,6 @@ double score(const Variant &v, const PlanData &p, const Hardware &hw, std::strin
   if (v.launcher == L_SKINNY && !skinny_shape_ok(p, why)) return -1.0;
   if (v.launcher != L_SKINNY && v.cfg.split_k > 1 && p.K < int64_t(2) * v.cfg.split_k * v.cfg.bk) {
     if (why) *why = "split-K variant needs at least two K slabs per chunk";
-    return -1.0;
-  }
-  if (v.launcher == L_BIG_256 && (p.layout & GEMM_A_COL)) {
-    if (why) *why = "256x256 four-wave variant needs row-major A";
     return -1.0;
   }
   if (needs_aligned_staging(v.launcher) &&

@@ -20,10 +20,6 @@ enum LauncherId {
   L_MFMA_128x128,
   L_MFMA_256x128,
   L_MFMA_256x256,
-  L_RING_256x256_W4,
-  L_RING_256x256_W8,
-  L_RING_128x128_W4,
-  L_BIG_256,
   L_SKINNY,
   L_W8_256,
   L_W8_128,
@@ -51,7 +47,7 @@ struct Variant {
   int fallback;       // LauncherId run instead when run-time checks rule this one out (-1: none)
 };
 
-// Ring variants (direct global-to-LDS loads) need 16-byte aligned operands whose
+// Variants with direct global-to-LDS loads need 16-byte aligned operands whose
 // contiguous extents and leading dimensions are multiples of 8 elements, and slab
 // offsets below 2^31 bytes.
 bool ring_shape_ok(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, bool a_col, bool b_col,

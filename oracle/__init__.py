@@ -47,6 +47,8 @@ def _load():
     lib.oracle_encode_bf16.argtypes = [ctypes.c_double]
     lib.oracle_encode_bf16.restype = ctypes.c_uint16
     lib.oracle_max_threads.restype = i32
+    lib.oracle_set_threads.argtypes = [i32]
+    lib.oracle_set_threads.restype = None
     _lib = lib
     return lib
 
@@ -142,6 +144,11 @@ def decode(bits, dtype):
 
 def max_threads():
     return int(_load().oracle_max_threads())
+
+
+def set_threads(n):
+    """Threads of the oracle's parallel loops from now on (results do not depend on it)."""
+    _load().oracle_set_threads(int(n))
 
 
 def epilogue(S, alpha=1.0, beta=0.0, C_prior=None, bias=None, activation="none"):

@@ -245,3 +245,15 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/* Thread count of the parallel loops above (timing of the oracle on a given number of
+ * host cores); n < 1 is taken as 1.  The results do not depend on it. */
+void oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n < 1 ? 1 : n);
+#else
+    (void)n;
+#endif
+}

@@ -233,3 +233,11 @@ def test_forced_eight_wave_split_needs_two_slabs_per_chunk():
         _plan(512, 512, 1024, mh.GEMM_BF16_BF16, cfg=(2, 64, 64, 128, 2, 4, 5, 8))
     d = _plan(512, 512, 2048, mh.GEMM_BF16_BF16, cfg=(2, 64, 64, 128, 2, 4, 5, 8))
     assert d["split_k"] == 8
+
+
+def test_clock_probe_argument_checks():
+    """gemm_clock_probe validates before touching a device."""
+    for out, ticks, msg in ((0, 100, "NULL"), (12, 100, "misaligned"), (16, 0, "ticks"),
+                            (16, 10 ** 9 + 1, "ticks")):
+        with pytest.raises(mh.GemmError, match=msg):
+            mh.gemm_clock_probe(out, ticks, stream=0)

@@ -97,3 +97,48 @@ def test_roofline_is_min_of_roofs():
     assert F.roofline(2.5e15, 8e12, 15.9) == pytest.approx(15.9 * 8e12)
     assert F.roofline(2.5e15, 8e12, 1365) == 2.5e15
     assert F.ridge_point(2.5e15, 8e12) == pytest.approx(312.5)
+
+
+def test_square_tile_intensity_is_the_tiled_intensity_of_a_square_tile():
+    """The qian.cx note's 0.5*b (b x b output tile, fp16) and the T_M x T_N formula of
+    "Tiling 策略与内存层次优化" are the same quantity for square tiles; both equal the
+    FLOPs over the counted loads of the tiled loop nest."""
+    for b in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        for e in (2, 4):
+            assert F.tiled_intensity_square(b, e) == pytest.approx(F.tiled_intensity(b, b, e), rel=1e-15)
+    for b in (2, 4, 8):
+        M = N = 2 * b
+        K = 6
+        loads = F.count_tiled_loads(M, N, K, b, b, 3)
+        assert F.gemm_flops(M, N, K) / (loads * 2) == pytest.approx(F.tiled_intensity_square(b, 2), rel=1e-12)
+
+
+def test_square_tile_scales_naive_intensity_by_b():
+    # qian.cx: tiling with b x b output tiles divides the loads by b, so the intensity
+    # is b times the naive one.
+    for b in (1, 3, 16, 249):
+        assert F.tiled_intensity_square(b, 2) == pytest.approx(b * F.naive_intensity(2))
+
+
+def test_compute_intensity_of_counted_loop_nests():
+    """FLOPs over counted bytes: the naive nest gives 1/elem, the tiled one the tile formula."""
+    M, N, K = 3, 5, 7
+    assert F.compute_intensity(F.gemm_flops(M, N, K), F.count_naive_loads(M, N, K) * 2) == 0.5
+    loads = F.count_tiled_loads(8, 8, 12, 8, 8, 4)
+    assert F.compute_intensity(F.gemm_flops(8, 8, 12), loads * 4) == pytest.approx(F.tiled_intensity(8, 8, 4))
+
+
+def test_roofline_switches_roofs_at_the_printed_ridge():
+    """Below the ridge the bandwidth roof binds, at and above it the compute roof.
+    A100: ridge 156 FLOP/B ("Tiling 策略与内存层次优化"); V100-class: b = 249 reaches the
+    compute roof and b = 248 does not (qian.cx: b >= 2P/B)."""
+    assert F.roofline(312e12, 2e12, 155) == pytest.approx(155 * 2e12)
+    assert F.roofline(312e12, 2e12, 155) < 312e12
+    assert F.roofline(312e12, 2e12, F.ridge_point(312e12, 2e12)) == 312e12
+    assert F.roofline(112e12, 900e9, F.tiled_intensity_square(248)) < 112e12
+    assert F.roofline(112e12, 900e9, F.tiled_intensity_square(249)) == 112e12
+    b_min = F.tile_needed_for_ridge(112e12, 900e9, 2)
+    assert F.roofline(112e12, 900e9, F.tiled_intensity_square(b_min)) == pytest.approx(112e12)
+    # monotone in intensity, flat above the ridge
+    vals = [F.roofline(2.5e15, 8e12, ai) for ai in (1, 10, 100, 312.5, 1000, 1365)]
+    assert vals == sorted(vals) and vals[-1] == vals[-2] == vals[-3] == 2.5e15

@@ -172,17 +172,8 @@ def test_workloads_with_epilogue(name):
     vals, _, desc = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col,
                             c_init=Cs, epi=epi)
     Cp = _prior(Cs, w.out)
-    if w.M * w.N * w.K <= 1 << 31:
-        S = oracle_ref(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.a_col, w.b_col)
-        check_tolerance(vals, oracle.epilogue(S, 0.5, 0.25, Cp, bias.numpy(), "relu"), w.out, name)
-        return
-    rng = np.random.default_rng(1)
-    ii = np.concatenate([rng.integers(0, w.M, 3000), [0, w.M - 1]])
-    jj = np.concatenate([rng.integers(0, w.N, 3000), [w.N - 1, 0]])
-    S = oracle.elements(w.M, w.N, w.K, synth.to_storage_numpy(As), lda, synth.to_storage_numpy(Bs), ldb,
-                        w.dtype, ii, jj, a_col=w.a_col, b_col=w.b_col)
-    ref = oracle.epilogue(S[None, :], 0.5, 0.25, Cp[ii, jj][None, :], bias.numpy()[jj], "relu")[0]
-    check_tolerance(vals[ii, jj], ref, w.out, f"{name} sampled")
+    S = oracle_ref(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.a_col, w.b_col)
+    check_tolerance(vals, oracle.epilogue(S, 0.5, 0.25, Cp, bias.numpy(), "relu"), w.out, name)
 
 
 # The 256 x 256 eight-wave tile brings a 16-bit prior C into LDS with the loads of the

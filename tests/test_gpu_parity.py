@@ -1,9 +1,7 @@
 """Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
 
 Workload tests run each measured shape at full size in the configuration the planner
-picks (the one the benchmark times) and compare every output the oracle can afford:
-whole matrices up to 1024^3, sampled rows at 2048^3, sampled elements at 4096^3, and
-the whole skinny product.  Then: ragged extents that leave partial tiles in every
+picks (the one the benchmark times) and compare every output with the oracle.  Then: ragged extents that leave partial tiles in every
 dimension, every compiled variant forced on a ragged shape, every layout, padded
 leading dimensions, misaligned pointers (narrow-load path), bit-exact small-integer
 suites (one pins the round-to-nearest-even epilogue), closed forms, degenerate
@@ -62,34 +60,46 @@ def test_workload_whole(name):
     check_tolerance(C, Cref, w.out, name)
 
 
-def test_workload_2048_nt_sampled_rows():
+def test_workload_2048_nt_whole():
     w, As, lda, Bs, ldb = _workload("f16_2048_nt")
     C, raw, desc = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col)
-    bm = desc["bm"]
-    rows = sorted({0, 1, w.M - 1} | {t * bm + o for t in range(0, w.M // bm, 3) for o in (0, bm - 1)})
-    for r in rows:
-        Cref = oracle_ref(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.a_col, w.b_col, rows=(r, r + 1))
-        check_tolerance(C[r:r + 1], Cref, w.out, f"row {r}")
+    Cref = oracle_ref(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.a_col, w.b_col)
+    check_tolerance(C, Cref, w.out, "f16_2048_nt")
+    # the elementwise bar as well, on every output (the normwise one could hide a few)
+    err = np.abs(C - Cref)
+    assert np.all(err <= 1e-3 * (np.abs(Cref) + 1.0)), float(err.max())
 
 
-def test_workload_4096_sampled_elements():
+def test_workload_4096_whole():
     w, As, lda, Bs, ldb = _workload("bf16_4096")
     C, raw, desc = run_gpu(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.out, w.a_col, w.b_col)
-    bm, bn = desc["bm"], desc["bn"]
-    rng = np.random.default_rng(0)
-    corners_i = [t * bm + o for t in range(w.M // bm) for o in (0, bm - 1)]
-    corners_j = [t * bn + o for t in range(w.N // bn) for o in (0, bn - 1)]
-    ci, cj = np.meshgrid(corners_i, corners_j, indexing="ij")
-    ii = np.concatenate([ci.reshape(-1), rng.integers(0, w.M, 12000)])
-    jj = np.concatenate([cj.reshape(-1), rng.integers(0, w.N, 12000)])
-    ref = oracle.elements(w.M, w.N, w.K, synth.to_storage_numpy(As), lda, synth.to_storage_numpy(Bs), ldb,
-                          w.dtype, ii, jj)
-    check_tolerance(C[ii, jj], ref, w.out, "sampled elements")
+    Cref = oracle_ref(As, lda, Bs, ldb, w.M, w.N, w.K, w.dtype, w.a_col, w.b_col)
+    check_tolerance(C, Cref, w.out, "bf16_4096")
+    # Where |C_ref| >= 1 a bf16 step (>= 2^-7) is far above the fp32 sums' error, so the
+    # result is the nearest bf16 of C_ref or a neighbour of it.
+    big = np.abs(Cref) >= 1.0
+    near = oracle.encode(Cref[big], "bf16").astype(np.int32)
+    assert np.all(np.abs(raw[big].astype(np.int32) - near) <= 1)
     # All-ones closed form over the whole output at the same shape: C_ij = K exactly.
     ones = torch.ones((w.M, w.K), dtype=synth.TORCH_DTYPES[w.dtype])
     onesb = torch.ones((w.K, w.N), dtype=synth.TORCH_DTYPES[w.dtype])
     C1, raw1, _ = run_gpu(ones, w.K, onesb, w.N, w.M, w.N, w.K, w.dtype, w.out)
     assert np.all(C1 == w.K)
+
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (2048, 1024, 8192)])
+def test_256_tile_both_k_contiguous_whole(M, N, K):
+    """The 256 x 256 tile with row-major A and column-major B (A in pairs of slabs, B
+    refilled in the phase of its last reads), forced, on random data at a deep K, every
+    output against the oracle."""
+    print(f"[256 tile NT whole] M={M} N={N} K={K}", flush=True)
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "bf16", b_col=True, seed=7)
+    C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "bf16", "f32", False, True, cfg=(2, 256, 256, 32, 2, 4, 5, 1))
+    assert (desc["bm"], desc["bn"]) == (256, 256)
+    Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16", False, True)
+    check_tolerance(C, Cref, "f32", "256 tile NT")
+    err = np.abs(C - Cref)
+    assert np.all(err <= 1e-3 * (np.abs(Cref) + 1.0)), float(err.max())
 
 
 def test_workload_64_as_two_by_two_tiles():
@@ -120,10 +130,7 @@ def test_ragged_extents(in_t, out_t):
             check_tolerance(C, Cref, out_t, f"M={M} N={N} K={K} a_col={a_col} b_col={b_col}")
 
 
-ALIGNED_ONLY = {(2, 128, 128, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 2, 4, 1), (2, 256, 256, 32, 2, 4, 4, 1),
-                (2, 256, 256, 64, 2, 2, 2, 1), (2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1),
-                (2, 64, 64, 128, 2, 4, 5, 1)}
-ROW_MAJOR_A_ONLY = {(2, 256, 256, 64, 2, 2, 2, 1)}
+ALIGNED_ONLY = {(2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1), (2, 64, 64, 128, 2, 4, 5, 1)}
 
 
 @pytest.mark.parametrize("in_t,out_t", ALL_DTYPES)
@@ -134,10 +141,6 @@ def test_every_variant_every_layout_ragged(in_t, out_t):
         M, N, K = (304, 272, 200) if cfg in ALIGNED_ONLY else (300, 270, 200)
         for a_col, b_col in LAYOUTS:
             As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, a_col, b_col, seed=3)
-            if a_col and cfg in ROW_MAJOR_A_ONLY:
-                with pytest.raises(mh.GemmError, match="row-major A"):
-                    run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, cfg=cfg)
-                continue
             C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, a_col, b_col, cfg=cfg)
             assert (desc["bm"], desc["bn"]) == (cfg[1], cfg[2])
             Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, a_col, b_col)
@@ -161,23 +164,6 @@ def test_aligned_variants_fall_back_on_misaligned_pointers(cfg, b_col):
     C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "bf16", "f32", False, b_col, cfg=cfg,
                            offset_a=1, offset_b=0)
     check_tolerance(C, oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16", False, b_col), "f32")
-
-
-BIG_256 = (2, 256, 256, 64, 2, 2, 2, 1)
-
-
-@pytest.mark.parametrize("in_t,out_t", [("bf16", "bf16"), ("f16", "f32"), ("bf16", "f32")])
-@pytest.mark.parametrize("b_col", [False, True])
-def test_four_wave_256_kernel_every_slab_count(in_t, out_t, b_col):
-    """The 256 x 256 four-wave kernel pipelines two 64-deep slabs per loop trip and
-    peels an odd last slab; K from one partial slab to five slabs, on a ragged grid."""
-    M, N = 264, 520
-    for K in (8, 64, 72, 136, 200, 320):
-        As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, False, b_col, seed=K)
-        C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t, False, b_col, cfg=BIG_256)
-        assert (desc["bm"], desc["bn"]) == (256, 256)
-        Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, in_t, False, b_col)
-        check_tolerance(C, Cref, out_t, f"K={K} b_col={b_col}")
 
 
 W8_256 = (2, 256, 256, 32, 2, 4, 5, 1)
@@ -413,3 +399,56 @@ def test_single_element_and_single_row():
             As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, in_t, seed=M + N + K)
             C, raw, _ = run_gpu(As, lda, Bs, ldb, M, N, K, in_t, out_t)
             check_tolerance(C, oracle_ref(As, lda, Bs, ldb, M, N, K, in_t), out_t, f"{M}x{N}x{K}")
+
+
+# ---- operands at addresses whose low 32 bits have bit 31 set --------------------------------
+# The eight-wave kernels read their load origins through the first lane, 32 bits at a
+# time; a low half with bit 31 set must not spill into the high half.  A is placed so
+# that it starts 512 KiB below a 4 GiB boundary (low word 0xFFF80000, bit 31 set, and
+# the operand crosses into the next 4 GiB), B at low word 0x80000100.
+
+def _place(storage, low_word, keep):
+    """Copy a CPU storage tensor into a fresh device buffer at the first address whose
+    low 32 bits equal `low_word`; returns that address (the buffer is kept alive in
+    `keep`)."""
+    flat = storage.reshape(-1)
+    nbytes = flat.numel() * flat.element_size()
+    buf = torch.empty((1 << 32) + nbytes + 4096, dtype=torch.uint8, device="cuda")
+    keep.append(buf)
+    base = buf.data_ptr()
+    off = (low_word - (base & 0xFFFFFFFF)) % (1 << 32)
+    assert off + nbytes <= buf.numel()
+    addr = base + off
+    assert addr & 0xFFFFFFFF == low_word and addr % 16 == 0
+    buf[off:off + nbytes].copy_(flat.contiguous().view(torch.uint8).to("cuda"))
+    return addr
+
+
+W8_CONFIGS = [(2, 256, 256, 32, 2, 4, 5, 1), (2, 128, 128, 64, 2, 4, 5, 1), (2, 64, 64, 128, 2, 4, 5, 1),
+              (2, 128, 128, 64, 2, 4, 5, 2)]
+
+
+@pytest.mark.parametrize("cfg", W8_CONFIGS)
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_operands_at_high_low_word(cfg, a_col, b_col):
+    M, N, K = 512, 512, 1024
+    print(f"[high low word] cfg={cfg} a_col={a_col} b_col={b_col}", flush=True)
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "bf16", a_col, b_col, dist="int", r=3, seed=31)
+    keep = []
+    try:
+        a_addr = _place(As, 0xFFF80000, keep)
+        b_addr = _place(Bs, 0x80000100, keep)
+        C = torch.full((M, N), float("nan"), dtype=torch.float32, device="cuda")
+        layout = (mh.GEMM_A_COL if a_col else 0) | (mh.GEMM_B_COL if b_col else 0)
+        plan = mh.gemm_plan_config(M, N, K, lda, ldb, N, mh.GEMM_BF16_F32, layout, cfg)
+        try:
+            mh.gemm_run(plan, a_addr, b_addr, C)
+            torch.cuda.synchronize()
+        finally:
+            mh.gemm_destroy(plan)
+        got = C.cpu().numpy()
+    finally:
+        del keep
+        torch.cuda.empty_cache()
+    Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16", a_col, b_col)
+    check_exact(got, Cref, "f32", f"cfg={cfg}")
