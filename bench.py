@@ -43,6 +43,8 @@ ROTATE_BYTES = 512 << 20       # working set of rotated operand copies, > 256 MB
 # instead of 105-115); these calls (~0.2 s) let it settle, so that the warm-up and the
 # timed steps see the steady state whatever --warmup the caller passes.
 SETTLE_CALLS = 2000
+# Spread of the call times: 30 groups of 10 consecutive calls.
+PER_CALL_GROUPS, PER_CALL_GROUP_SIZE = 30, 10
 # Window of the clock probe: 2,000,000 ticks of the 100 MHz real-time counter (20 ms).
 CLOCK_TICKS = 2_000_000
 
@@ -150,14 +152,18 @@ def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock
         event_ms = ev0.elapsed_time(ev1) / steps
         calls = []
         if per_call:
+            # The spread between calls: HIP events around each of 30 groups of 10
+            # consecutive calls (an event pair around every single call would add its own
+            # gap to every call), each group's mean per call.
             evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(steps)]
-            for i, (a, b) in enumerate(evs):
+                   for _ in range(PER_CALL_GROUPS)]
+            for g, (a, b) in enumerate(evs):
                 a.record(stream)
-                run(i)
+                for i in range(PER_CALL_GROUP_SIZE):
+                    run(g * PER_CALL_GROUP_SIZE + i)
                 b.record(stream)
             torch.cuda.synchronize()
-            calls = sorted(a.elapsed_time(b) for a, b in evs)
+            calls = sorted(a.elapsed_time(b) / PER_CALL_GROUP_SIZE for a, b in evs)
         clock_mhz = clock_during(run, steps) if clock else None
     finally:
         mh.gemm_destroy(plan)
@@ -442,6 +448,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the fused-epilogue line and the autotune sweep report")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--settle", type=int, default=SETTLE_CALLS,
+                    help="untimed calls of the headline plan before its warm-up (profiled runs: 0)")
+    ap.add_argument("--no-clock", action="store_true", help="skip the clock probe (profiled runs)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after timing, run one elementwise kernel of known traffic (counter scale)")
     ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "DIGEST"),
@@ -462,11 +471,12 @@ def main():
     torch.cuda.set_device(0)
     log(f"[bench] device {torch.cuda.get_device_name(0)}; headline {args.workload}")
 
-    head = measure(args.workload, args.steps, args.warmup, settle=SETTLE_CALLS, per_call=True, clock=True)
+    head = measure(args.workload, args.steps, args.warmup, settle=args.settle, per_call=True,
+                   clock=not args.no_clock)
     log(f"[bench] headline {head['workload']}: {head['tflops']:.1f} TFLOP/s "
         f"({head['ms_per_step'] * 1000:.1f} us/step, kernel {head['kernel_ms_event'] * 1000:.1f} us, "
         f"per call p10/p50/p90 {[round(1000 * v, 1) for v in head.get('kernel_ms_p10_p50_p90', [])]} us, "
-        f"clock {head['clock_mhz']:.0f} MHz)")
+        f"clock {head.get('clock_mhz', float('nan')):.0f} MHz)")
     shapes = []
     if not args.no_per_shape:
         for name in PER_SHAPE:
@@ -511,11 +521,11 @@ def main():
         "roofline": {"bound": "mfma" if w.dtype != "f32" else "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak, "traffic": traffic},
         "cpu_baseline": cpu,
-        "clock_mhz": round(head["clock_mhz"], 1),
+        "clock_mhz": round(head["clock_mhz"], 1) if "clock_mhz" in head else None,
         "clock_note": "average shader clock over 20 ms of further headline calls (s_memtime over "
                       "s_memrealtime on a one-wave probe on a second stream)",
         "kernel_ms_p10_p50_p90": head.get("kernel_ms_p10_p50_p90"),
-        "settle_calls": SETTLE_CALLS,
+        "settle_calls": args.settle,
         "kernel_source_digest": kernel_source_digest(),
         "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                       for r in shapes],
