@@ -173,6 +173,25 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C,
                       const gemm_epilogue_t *epi, void *stream);
 
 /*
+ * gemm_run_noalloc -- gemm_run_epilogue for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the problem is planned on the host as gemm_plan would plan it (tuned
+ * table first, then the selector) and run at once, with no plan object.  A split-K
+ * plan's workspace (arrival counters and fp32 partial sums) lives in a 16 MiB array
+ * of device memory that the library holds on every GPU it runs on until the process
+ * ends; nothing is allocated per call (the first call on a device looks up the
+ * array's address there).  A plan whose workspace exceeds 16 MiB is rejected with
+ * GEMM_ERR_UNSUPPORTED and a message.  All calls on one GPU share that array: calls
+ * that may overlap in time on one GPU (different streams, or different threads) race
+ * and give wrong results when their plans use split-K; serialise them.  Arguments
+ * are those of gemm_plan followed by those of gemm_run_epilogue (epi may be NULL);
+ * same results bit for bit as gemm_plan + gemm_run_epilogue, same status codes, plus
+ * GEMM_ERR_INVALID_ARG for a problem gemm_plan rejects.  Asynchronous on `stream`.
+ */
+int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+                     int layout, const void *A, const void *B, void *C, const gemm_epilogue_t *epi, void *stream);
+
+/*
  * gemm_transpose -- out = transpose of in, the second tiled workload of "CUDA tile"
  * (applications section: a tile staged through shared memory makes both the reads
  * and the writes of a transpose coalesced):

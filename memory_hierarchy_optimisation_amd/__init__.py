@@ -40,7 +40,8 @@ DESCRIBE_FIELDS = ("kind", "bm", "bn", "bk", "waves_m", "waves_n", "stages", "sp
 
 EXPORTS = ("gemm_plan", "gemm_plan_config", "gemm_run", "gemm_run_epilogue", "gemm_destroy",
            "gemm_last_error", "gemm_plan_describe", "gemm_catalogue", "gemm_autotune", "gemm_tune_save",
-           "gemm_tune_load", "gemm_tune_clear", "gemm_transpose", "gemm_clock_probe")
+           "gemm_tune_load", "gemm_tune_clear", "gemm_transpose", "gemm_clock_probe",
+           "gemm_run_noalloc")
 
 
 class Epilogue(ctypes.Structure):
@@ -103,6 +104,9 @@ def _load():
     lib.gemm_tune_clear.restype = None
     lib.gemm_transpose.argtypes = [vp, vp, i64, i64, i64, i64, i32, vp]
     lib.gemm_transpose.restype = i32
+    lib.gemm_run_noalloc.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp,
+                                     ctypes.POINTER(Epilogue), vp]
+    lib.gemm_run_noalloc.restype = i32
     lib.gemm_clock_probe.argtypes = [vp, i64, vp]
     lib.gemm_clock_probe.restype = i32
     runtimes = hip_runtimes_mapped()
@@ -240,5 +244,16 @@ def gemm_clock_probe(out, ticks, stream=None):
     """Enqueue the one-wave clock probe: out (device, two uint64) receives the shader
     cycles and the 100 MHz real-time ticks of a window of `ticks` ticks."""
     rc = _lib.gemm_clock_probe(_ptr(out), int(ticks), _stream(stream))
+    if rc != GEMM_OK:
+        raise GemmError(rc, gemm_last_error())
+
+
+def gemm_run_noalloc(M, N, K, lda, ldb, ldc, dtype, layout, A, B, C, alpha=1.0, beta=0.0, bias=None,
+                     activation=GEMM_ACT_NONE, stream=None, epilogue=False):
+    """Plan and run in one call with no device allocation (split-K workspaces in the
+    library's per-GPU scratch array).  epilogue=False passes no epilogue (gemm_run)."""
+    epi = ctypes.byref(Epilogue(float(alpha), float(beta), _ptr(bias), int(activation))) if epilogue else None
+    rc = _lib.gemm_run_noalloc(M, N, K, lda, ldb, ldc, dtype, layout, _ptr(A), _ptr(B), _ptr(C), epi,
+                               _stream(stream))
     if rc != GEMM_OK:
         raise GemmError(rc, gemm_last_error())

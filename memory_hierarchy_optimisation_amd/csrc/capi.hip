@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -57,13 +58,15 @@ mhg::Hardware query_hardware() {
 // padded to 256 bytes).
 int64_t counter_words(const mhg::PlanData &d) { return (int64_t(d.gn) * 4 + 255) / 256 * 64; }
 
-gemm_plan_t make_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
-                      int dtype, int layout, const int32_t *cfg) {
+// Validate a problem and choose its configuration (forced, tuned or by the selector):
+// host work only, nothing allocated on a device.  False with the message set.
+bool choose_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype, int layout,
+                 const int32_t *cfg, mhg::PlanData *out) {
   mhg::PlanData d;
   std::string err;
   if (!mhg::validate(M, N, K, lda, ldb, ldc, dtype, layout, &d, &err)) {
     set_error(err);
-    return nullptr;
+    return false;
   }
   const mhg::Hardware hw = query_hardware();
   // A configuration measured fastest for exactly this problem (gemm_autotune, or a
@@ -86,8 +89,16 @@ gemm_plan_t make_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb,
   }
   if (!ok) {
     set_error(err);
-    return nullptr;
+    return false;
   }
+  *out = d;
+  return true;
+}
+
+gemm_plan_t make_plan(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc,
+                      int dtype, int layout, const int32_t *cfg) {
+  mhg::PlanData d;
+  if (!choose_plan(M, N, K, lda, ldb, ldc, dtype, layout, cfg, &d)) return nullptr;
   gemm_plan_s *plan = new (std::nothrow) gemm_plan_s;
   if (!plan) {
     set_error("gemm_plan: out of host memory");
@@ -143,6 +154,52 @@ int ensure_workspace(gemm_plan_s *plan, hipStream_t s) {
   return GEMM_OK;
 }
 
+// Scratch memory of the allocation-free entry point (gemm_run_noalloc): the split-K
+// workspaces its plans need, in a file-scope device array that each GPU holds from
+// the library's load until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol): its address on each
+// device is asked once, with that device current, and kept here.
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's scratch address, looked up on its first use.  Returns a gemm_status.
+int scratch_of_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    set_error("gemm_run_noalloc: no current HIP device");
+    return GEMM_ERR_HIP;
+  }
+  if (dev >= kMaxDevices) {
+    set_error("gemm_run_noalloc: device index beyond the 64 this library keeps scratch addresses for");
+    return GEMM_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      set_error(std::string("gemm_run_noalloc: cannot find the scratch array on the device: ") +
+                hipGetErrorString(e));
+      return GEMM_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GEMM_OK;
+}
+
+// Enqueue a chosen plan.  The split-K workspace comes from `plan` (allocated on its
+// first run when gemm_plan could not) or, with plan == NULL, from the device's scratch
+// array, whose arrival counters are cleared first by a fill kernel.
+int run_chosen(const mhg::PlanData &d, gemm_plan_s *plan, const void *A, const void *B, void *C,
+               const gemm_epilogue_t *epi, hipStream_t s);
+
 }  // namespace
 
 namespace mhg {
@@ -169,12 +226,12 @@ int gemm_run(gemm_plan_t plan, const void *A, const void *B, void *C, void *stre
   return gemm_run_epilogue(plan, A, B, C, nullptr, stream);
 }
 
-int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, const gemm_epilogue_t *epi,
-                      void *stream) {
-  if (!plan) {
-    set_error("gemm_run: NULL plan");
-    return GEMM_ERR_INVALID_ARG;
-  }
+}  // extern "C"
+
+namespace {
+
+int run_chosen(const mhg::PlanData &d, gemm_plan_s *plan, const void *A, const void *B, void *C,
+               const gemm_epilogue_t *epi, hipStream_t s) {
   if (epi && epi->activation != GEMM_ACT_NONE && epi->activation != GEMM_ACT_RELU) {
     set_error("gemm_run_epilogue: unknown activation");
     return GEMM_ERR_INVALID_ARG;
@@ -183,7 +240,6 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
     set_error("gemm_run_epilogue: bias must be 4-byte aligned fp32");
     return GEMM_ERR_INVALID_ARG;
   }
-  const mhg::PlanData &d = plan->d;
   if (d.M == 0 || d.N == 0) return GEMM_OK;
   if (!C) {
     set_error("gemm_run: NULL C");
@@ -216,7 +272,6 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
     a.act = epi->activation;
     a.epi = !(a.alpha == 1.0f && a.beta == 0.0f && !a.bias && a.act == GEMM_ACT_NONE);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (d.K == 0) {
     e = mhg::launch_fill(a, s);
@@ -245,9 +300,25 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
       a.split_k = 1;
     }
     if (a.split_k > 1) {
-      const int st = ensure_workspace(plan, s);
-      if (st != GEMM_OK) return st;
-      a.workspace = plan->ws;
+      if (plan) {
+        const int st = ensure_workspace(plan, s);
+        if (st != GEMM_OK) return st;
+        a.workspace = plan->ws;
+      } else {
+        if (d.ws_bytes > kScratchBytes) {
+          set_error("gemm_run_noalloc: the plan's split-K workspace (" + std::to_string(d.ws_bytes) +
+                    " bytes) exceeds the scratch array (" + std::to_string(kScratchBytes) + " bytes)");
+          return GEMM_ERR_UNSUPPORTED;
+        }
+        const int st = scratch_of_current_device(&a.workspace);
+        if (st != GEMM_OK) return st;
+        // The skinny kernel's arrival counters must start at zero; the array keeps
+        // whatever the previous call on this device left there.
+        if (v->launcher == mhg::L_SKINNY && mhg::launch_zero_words(a.workspace, counter_words(d), s) != hipSuccess) {
+          set_error("gemm_run_noalloc: cannot clear the arrival counters");
+          return GEMM_ERR_HIP;
+        }
+      }
       a.ws_bytes = d.ws_bytes;
       // Eight-wave split-K: K per chunk, a whole number of slabs.
       const int64_t bk = v->cfg.bk, per = (d.K + a.split_k - 1) / a.split_k;
@@ -271,6 +342,26 @@ int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, c
     return GEMM_ERR_HIP;
   }
   return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gemm_run_epilogue(gemm_plan_t plan, const void *A, const void *B, void *C, const gemm_epilogue_t *epi,
+                      void *stream) {
+  if (!plan) {
+    set_error("gemm_run: NULL plan");
+    return GEMM_ERR_INVALID_ARG;
+  }
+  return run_chosen(plan->d, plan, A, B, C, epi, static_cast<hipStream_t>(stream));
+}
+
+int gemm_run_noalloc(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
+                     int layout, const void *A, const void *B, void *C, const gemm_epilogue_t *epi, void *stream) {
+  mhg::PlanData d;
+  if (!choose_plan(M, N, K, lda, ldb, ldc, dtype, layout, nullptr, &d)) return GEMM_ERR_INVALID_ARG;
+  return run_chosen(d, nullptr, A, B, C, epi, static_cast<hipStream_t>(stream));
 }
 
 void gemm_destroy(gemm_plan_t plan) {

@@ -241,3 +241,19 @@ def test_clock_probe_argument_checks():
                             (16, 10 ** 9 + 1, "ticks")):
         with pytest.raises(mh.GemmError, match=msg):
             mh.gemm_clock_probe(out, ticks, stream=0)
+
+
+def test_noalloc_rejects_a_workspace_beyond_its_scratch(tmp_path):
+    """A plan whose split-K workspace exceeds the 16 MiB scratch array is refused with a
+    message before anything reaches a device (the tuned table forces such a plan:
+    2048 x 2048 partials of fp32 in 8 chunks are 128 MiB)."""
+    table = tmp_path / "tune.txt"
+    table.write_text("2048 2048 8192 8192 2048 2048 4 0 | 2 128 128 64 2 4 5 8 | 1.0\n")
+    assert mh.gemm_tune_load(str(table)) == 1
+    try:
+        with pytest.raises(mh.GemmError, match="exceeds the scratch array"):
+            mh.gemm_run_noalloc(2048, 2048, 8192, 8192, 2048, 2048, mh.GEMM_BF16_F32, 0, 256, 256, 256, stream=0)
+        with pytest.raises(mh.GemmError, match="lda"):
+            mh.gemm_run_noalloc(16, 16, 16, 8, 16, 16, mh.GEMM_BF16_F32, 0, 256, 256, 256, stream=0)
+    finally:
+        mh.gemm_tune_clear()
