@@ -281,7 +281,7 @@ def copy_reference(nbytes=512 << 20):
 def traffic_for(name):
     """HBM bytes per launch from the committed counter summary, if it was taken on the
     current kernel sources; otherwise None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{name}.txt")
+    path = os.path.join(ROOT, "profiles", f"counters_{name}.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -298,65 +298,157 @@ def traffic_for(name):
         return None
 
 
-def summarize_traffic(fetch_csv, write_csv, name, digest, out_path):
-    """Write the HBM-traffic summary of one workload's GEMM kernel from two rocprofv3
-    counter runs (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch), each scaled by what
-    the same counter reads for the copy reference kernel of known traffic."""
+PROFILE_CMD = ("python3 bench.py --workload {w} --no-cpu-baseline --no-per-shape --steps 20 --warmup 2 "
+               "--settle 0 --no-clock --copy-reference")
+COUNTER_PASSES = {
+    "mfma": "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+            "SQ_CYCLES GRBM_GUI_ACTIVE GRBM_COUNT",
+    "lds": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_LDS_ADDR_CONFLICT SQ_INSTS_LDS GRBM_GUI_ACTIVE",
+    "fetch": "FETCH_SIZE",
+    "write": "WRITE_SIZE",
+}
+XCDS, SES, SIMDS = 8, 32, 1024     # MI355X: 8 XCDs, 4 shader engines each, 256 CUs x 4 SIMDs
+
+
+def summarize_counters(name, digest, csvs, out_path):
+    """Write profiles/counters_<workload>.txt from the four rocprofv3 counter runs of one
+    workload (COUNTER_PASSES, CSV output): per dispatch of its GEMM kernel, the matrix
+    work done and the matrix pipes' busy cycles, the clock, LDS bank conflicts, HBM
+    traffic (FETCH_SIZE / WRITE_SIZE scaled by what they read for the copy reference of
+    known traffic) and the registers of the kernel as loaded."""
     import csv
 
     import synth
 
-    def per_kernel(path):
-        acc = {}
+    per = {}        # pass -> kernel -> counter -> [values]
+    dur = {}        # kernel -> [ns] (each pass's dispatches; the profiler serialises them)
+    regs = {}
+    for tag, path in csvs.items():
+        acc = per.setdefault(tag, {})
         with open(path) as fh:
             for r in csv.DictReader(fh):
-                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return {k: sum(v) / len(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+                k = r["Kernel_Name"]
+                acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+                if tag == "mfma" and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    dur.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                regs[k] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["Scratch_Size"],
+                           r["LDS_Block_Size"])
+    kernels = [k for k in per["mfma"] if "mhg::" in k and "gemm" in k and "reduce" not in k]
+    if len(kernels) != 1:
+        raise SystemExit(f"expected one GEMM kernel in the profiled run, got {kernels}")
+    g = kernels[0]
+    ref = [k for k in per["fetch"] if "elementwise" in k and "Unary" in k]
+    if len(ref) != 1:
+        raise SystemExit(f"expected one copy reference kernel, got {ref}")
+    c = ref[0]
 
-    fetch, n_fetch = per_kernel(fetch_csv)
-    write, n_write = per_kernel(write_csv)
-    gemm = [k for k in fetch if "mhg::" in k and "gemm" in k]
-    ref = [k for k in fetch if "elementwise" in k and "Unary" in k]
-    if len(gemm) != 1 or len(ref) != 1:
-        raise SystemExit(f"expected one GEMM kernel and one copy reference, got {gemm} / {ref}")
-    g, c = gemm[0], ref[0]
-    ref_kib = (512 << 20) / 1024.0
-    f_scale, w_scale = ref_kib / fetch[c], ref_kib / write[c]
+    def mean(tag, k, counter):
+        v = per[tag][k][counter]
+        return sum(v) / len(v), len(v)
+
     w = synth.WORKLOADS[name]
-    _, alg = algorithmic(w)
-    traffic = fetch[g] * f_scale * 1024 + write[g] * w_scale * 1024
+    flops, alg = algorithmic(w)
+    ns = sum(dur[g]) / len(dur[g])
+    mops = mean("mfma", g, "SQ_INSTS_VALU_MFMA_MOPS_BF16")[0] + mean("mfma", g, "SQ_INSTS_VALU_MFMA_MOPS_F16")[0]
+    busy, n_disp = mean("mfma", g, "SQ_VALU_MFMA_BUSY_CYCLES")
+    gui = mean("mfma", g, "GRBM_GUI_ACTIVE")[0]
+    sq_busy = mean("mfma", g, "SQ_BUSY_CYCLES")[0]
+    gui_xcd = gui / XCDS
+    conflict = mean("lds", g, "SQ_LDS_BANK_CONFLICT")[0]
+    active = mean("lds", g, "SQ_LDS_IDX_ACTIVE")[0]
+    addr_conflict = mean("lds", g, "SQ_LDS_ADDR_CONFLICT")[0]
+    lds_insts = mean("lds", g, "SQ_INSTS_LDS")[0]
+    ref_kib = (512 << 20) / 1024.0
+    f_scale = ref_kib / mean("fetch", c, "FETCH_SIZE")[0]
+    w_scale = ref_kib / mean("write", c, "WRITE_SIZE")[0]
+    fetch_kib = mean("fetch", g, "FETCH_SIZE")[0]
+    write_kib = mean("write", g, "WRITE_SIZE")[0]
+    traffic = fetch_kib * f_scale * 1024 + write_kib * w_scale * 1024
+    vgpr, agpr, sgpr, scratch, lds = regs[g]
     lines = [
-        f"# HBM traffic per launch of the {name} GEMM kernel (rocprofv3 counters)",
+        f"# Counters of the {name} GEMM kernel ({w.note}), rocprofv3, per dispatch",
         f"kernel: {g}",
         f"kernel_source_digest: {digest}",
-        f"fetch_size_kib_per_dispatch: {fetch[g]:.1f}  (mean of {n_fetch[g]} dispatches)",
-        f"write_size_kib_per_dispatch: {write[g]:.1f}  (mean of {n_write[g]} dispatches)",
-        f"copy_reference_fetch_kib: {fetch[c]:.1f}  (kernel reads 524288 KiB)",
-        f"copy_reference_write_kib: {write[c]:.1f}  (kernel writes 524288 KiB)",
-        f"fetch_scale: {f_scale:.5f}",
-        f"write_scale: {w_scale:.5f}",
+        f"dispatches: {n_disp}",
+        f"duration_us_under_counters: {ns / 1000:.2f}  (dispatches serialised by the profiler)",
+        f"mfma_flop_per_dispatch: {mops * 512:.6g}  (SQ_INSTS_VALU_MFMA_MOPS_* x 512; 2MNK = {flops:.6g})",
+        f"achieved_tflops_under_counters: {mops * 512 / ns / 1e3:.1f}",
+        f"mfma_busy_cycles_per_simd: {busy / SIMDS:.0f}  (SQ_VALU_MFMA_BUSY_CYCLES over {SIMDS} SIMDs)",
+        f"gpu_active_cycles: {gui_xcd:.0f}  (GRBM_GUI_ACTIVE per XCD)",
+        f"mfma_busy_fraction: {busy / SIMDS / gui_xcd:.3f}  (busy cycles per SIMD over active cycles)",
+        f"clock_mhz_grbm: {gui_xcd / ns * 1e3:.0f}  (GRBM_GUI_ACTIVE per XCD over the dispatch duration)",
+        f"clock_mhz_sq_lower_bound: {sq_busy / SES / ns * 1e3:.0f}  (SQ_BUSY_CYCLES per shader engine; counts "
+        "only cycles with waves present)",
+        f"lds_bank_conflict_cycles: {conflict:.0f}",
+        f"lds_active_cycles: {active:.0f}",
+        f"lds_bank_conflicts_per_access: {conflict / max(active - conflict, 1.0):.4f}  (conflict cycles over "
+        "conflict-free LDS cycles)",
+        f"lds_address_conflict_cycles: {addr_conflict:.0f}",
+        f"lds_instructions: {lds_insts:.0f}",
+        f"fetch_size_kib: {fetch_kib:.1f}",
+        f"write_size_kib: {write_kib:.1f}",
+        f"fetch_scale: {f_scale:.4f}  (copy reference: {mean('fetch', c, 'FETCH_SIZE')[0]:.1f} KiB counted for "
+        "524288 KiB read)",
+        f"write_scale: {w_scale:.4f}  (copy reference: {mean('write', c, 'WRITE_SIZE')[0]:.1f} KiB counted for "
+        "524288 KiB written)",
         f"traffic_bytes_per_launch: {traffic:.0f}",
         f"algorithmic_bytes_per_launch: {alg:.0f}",
         f"traffic_over_algorithmic: {traffic / alg:.3f}",
-        "# commands (run from /tmp with TMPDIR=/tmp), each its own run:",
-        "#   rocprofv3 --pmc FETCH_SIZE -d gpurun_out/prof_fetch -o f -- python3 bench.py --no-cpu-baseline "
-        "--no-per-shape --steps 20 --warmup 2 --copy-reference",
-        "#   rocprofv3 --pmc WRITE_SIZE -d gpurun_out/prof_write -o w -- python3 bench.py --no-cpu-baseline "
-        "--no-per-shape --steps 20 --warmup 2 --copy-reference",
-        "#   rocpd2csv -i gpurun_out/prof_fetch/f_results.db -d pmc_csv/fetch ; "
-        "rocpd2csv -i gpurun_out/prof_write/w_results.db -d pmc_csv/write",
-        f"#   python3 bench.py --workload {name} --summarize-traffic pmc_csv/fetch/out_counter_collection_trace.csv "
-        "pmc_csv/write/out_counter_collection_trace.csv <kernel_source_digest>",
-        "# The copy reference is torch's elementwise multiply over 512 MiB (reads and writes 524288 KiB):",
-        f"# FETCH_SIZE reads {fetch[c] / ref_kib:.2f} of the bytes read (scale {f_scale:.2f}), "
-        f"WRITE_SIZE {write[c] / ref_kib:.2f} of the bytes written (scale {w_scale:.2f}).",
+        f"registers: vgpr={vgpr} agpr={agpr} sgpr={sgpr} scratch_bytes={scratch} lds_bytes={lds}",
+        "# commands, each a run of its own, from /tmp with TMPDIR=/tmp (R = the repository root):",
     ]
-    if name == "bf16_4096":
-        lines += ["# Each XCD owns a 4 x 8 block of the 16 x 16 tiles, so every A panel is fetched by 2 XCDs and",
-                  "# every B panel by 4: 96 panels of 2 MiB = 192 MiB, the fetch above."]
+    for tag, counters in COUNTER_PASSES.items():
+        lines.append(f"#   timeout -s KILL 300 rocprofv3 --pmc {counters} --output-format csv -d R/gpurun_out/pmc_{name}_{tag} "
+                     f"-o p -- {PROFILE_CMD.format(w=name).replace('bench.py', 'R/bench.py')}")
+    lines.append(f"#   python3 bench.py --workload {name} --summarize-counters <digest> "
+                 + " ".join(f"gpurun_out/pmc_{name}_{t}/p_counter_collection.csv" for t in COUNTER_PASSES))
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     log("\n".join(lines))
+
+
+def summarize_trace(trace_csv, digest, out_path, settle, warmup, steps, workload):
+    """Write profiles/kernel_trace_bench_default.txt from the kernel trace of a default
+    bench run: per kernel, dispatches and mean / min / max duration, and for the
+    headline kernel the mean over the timed calls (the first `settle` + `warmup`
+    dispatches of it are untimed; the next `steps` are the timed batch)."""
+    import csv
+
+    durs, order = {}, []
+    with open(trace_csv) as fh:
+        for r in csv.DictReader(fh):
+            k = r["Kernel_Name"]
+            if k not in durs:
+                durs[k] = []
+                order.append(k)
+            durs[k].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    for k in durs:
+        durs[k].sort()
+    rows = sorted(durs, key=lambda k: -sum(d for _, d in durs[k]))
+    head = [k for k in rows if "mhg::" in k and "gemm" in k]
+    hk = max(head, key=lambda k: len(durs[k]))
+    timed = [d for _, d in durs[hk][settle + warmup:settle + warmup + steps]]
+    lines = [
+        "# Kernel durations of a default bench.py run (rocprofv3 kernel trace)",
+        f"# kernel_source_digest: {digest}",
+        "# command (from /tmp with TMPDIR=/tmp; R = the repository root):",
+        "#   timeout -s KILL 900 rocprofv3 --kernel-trace --stats --output-format csv -d R/gpurun_out/prof_kt -o kt "
+        "-- python3 R/bench.py",
+        f"#   python3 bench.py --summarize-trace gpurun_out/prof_kt/kt_kernel_trace.csv {digest}",
+        f"# Headline kernel ({workload}): {hk}",
+        f"# Its dispatches in the order made: {settle} settling calls, {warmup} warm-up calls, {steps} timed calls "
+        "(HIP events around the batch), then 300 calls in groups of 10 and 600 beside the clock probe; later "
+        "dispatches of it belong to the fused-epilogue line (other flags) or the autotune sweep.",
+        f"headline_timed_mean_ns: {sum(timed) / max(len(timed), 1):.0f}  (dispatches {settle + warmup + 1} .. "
+        f"{settle + warmup + steps} of it)",
+        "KERNELS (name | dispatches | mean ns | min ns | max ns):",
+    ]
+    for k in rows:
+        d = [x for _, x in durs[k]]
+        lines.append(f"{k} | {len(d)} | {sum(d) / len(d):.0f} | {min(d)} | {max(d)}")
+    with open(out_path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    log("\n".join(lines[:12]))
 
 
 def cpu_model():
@@ -453,13 +545,20 @@ def main():
     ap.add_argument("--no-clock", action="store_true", help="skip the clock probe (profiled runs)")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after timing, run one elementwise kernel of known traffic (counter scale)")
-    ap.add_argument("--summarize-traffic", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "DIGEST"),
-                    help="write profiles/traffic_<workload>.txt from two counter runs and exit")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "DIGEST"),
+                    help="write profiles/kernel_trace_bench_default.txt from the kernel trace of a default run")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("DIGEST", "MFMA_CSV", "LDS_CSV", "FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/counters_<workload>.txt from the four counter runs and exit")
     args = ap.parse_args()
-    if args.summarize_traffic:
-        f, wcsv, digest = args.summarize_traffic
-        summarize_traffic(f, wcsv, args.workload, digest,
-                          os.path.join(ROOT, "profiles", f"traffic_{args.workload}.txt"))
+    if args.summarize_trace:
+        tcsv, digest = args.summarize_trace
+        summarize_trace(tcsv, digest, os.path.join(ROOT, "profiles", "kernel_trace_bench_default.txt"),
+                        args.settle, args.warmup, args.steps, args.workload)
+        return
+    if args.summarize_counters:
+        digest, *paths = args.summarize_counters
+        summarize_counters(args.workload, digest, dict(zip(COUNTER_PASSES, paths)),
+                           os.path.join(ROOT, "profiles", f"counters_{args.workload}.txt"))
         return
     if args.gpus != 1:
         log(f"bench.py measures one GPU: the product runs on a single MI355X, and sharding it over "
