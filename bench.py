@@ -298,6 +298,20 @@ def traffic_for(name):
         return None
 
 
+def build_resources():
+    """The compiler's per-kernel resource report of the in-tree build, keyed by the
+    demangled kernel name: {vgpr, agpr, sgpr, scratch, occupancy, lds, vgpr_spill}."""
+    import subprocess
+
+    path = os.path.join(ROOT, "_build", "resource_usage.txt")
+    if not os.path.exists(path):
+        return {}
+    rows = [line.split() for line in open(path) if line.strip()]
+    names = subprocess.run(["c++filt"], input="\n".join(r[0] for r in rows), capture_output=True,
+                           text=True).stdout.splitlines()
+    return {n: dict(kv.split("=", 1) for kv in r[1:]) for n, r in zip(names, rows)}
+
+
 PROFILE_CMD = ("python3 bench.py --workload {w} --no-cpu-baseline --no-per-shape --steps 20 --warmup 2 "
                "--settle 0 --no-clock --copy-reference")
 COUNTER_PASSES = {
@@ -322,7 +336,6 @@ def summarize_counters(name, digest, csvs, out_path):
 
     per = {}        # pass -> kernel -> counter -> [values]
     dur = {}        # kernel -> [ns] (each pass's dispatches; the profiler serialises them)
-    regs = {}
     for tag, path in csvs.items():
         acc = per.setdefault(tag, {})
         with open(path) as fh:
@@ -331,8 +344,6 @@ def summarize_counters(name, digest, csvs, out_path):
                 acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
                 if tag == "mfma" and r["Counter_Name"] == "GRBM_GUI_ACTIVE":
                     dur.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-                regs[k] = (r["VGPR_Count"], r["Accum_VGPR_Count"], r["SGPR_Count"], r["Scratch_Size"],
-                           r["LDS_Block_Size"])
     kernels = [k for k in per["mfma"] if "mhg::" in k and "gemm" in k and "reduce" not in k]
     if len(kernels) != 1:
         raise SystemExit(f"expected one GEMM kernel in the profiled run, got {kernels}")
@@ -351,9 +362,8 @@ def summarize_counters(name, digest, csvs, out_path):
     ns = sum(dur[g]) / len(dur[g])
     mops = mean("mfma", g, "SQ_INSTS_VALU_MFMA_MOPS_BF16")[0] + mean("mfma", g, "SQ_INSTS_VALU_MFMA_MOPS_F16")[0]
     busy, n_disp = mean("mfma", g, "SQ_VALU_MFMA_BUSY_CYCLES")
-    gui = mean("mfma", g, "GRBM_GUI_ACTIVE")[0]
     sq_busy = mean("mfma", g, "SQ_BUSY_CYCLES")[0]
-    gui_xcd = gui / XCDS
+    wave_cycles = sq_busy / SES
     conflict = mean("lds", g, "SQ_LDS_BANK_CONFLICT")[0]
     active = mean("lds", g, "SQ_LDS_IDX_ACTIVE")[0]
     addr_conflict = mean("lds", g, "SQ_LDS_ADDR_CONFLICT")[0]
@@ -364,7 +374,7 @@ def summarize_counters(name, digest, csvs, out_path):
     fetch_kib = mean("fetch", g, "FETCH_SIZE")[0]
     write_kib = mean("write", g, "WRITE_SIZE")[0]
     traffic = fetch_kib * f_scale * 1024 + write_kib * w_scale * 1024
-    vgpr, agpr, sgpr, scratch, lds = regs[g]
+    res = build_resources().get(g, {})
     lines = [
         f"# Counters of the {name} GEMM kernel ({w.note}), rocprofv3, per dispatch",
         f"kernel: {g}",
@@ -374,11 +384,12 @@ def summarize_counters(name, digest, csvs, out_path):
         f"mfma_flop_per_dispatch: {mops * 512:.6g}  (SQ_INSTS_VALU_MFMA_MOPS_* x 512; 2MNK = {flops:.6g})",
         f"achieved_tflops_under_counters: {mops * 512 / ns / 1e3:.1f}",
         f"mfma_busy_cycles_per_simd: {busy / SIMDS:.0f}  (SQ_VALU_MFMA_BUSY_CYCLES over {SIMDS} SIMDs)",
-        f"gpu_active_cycles: {gui_xcd:.0f}  (GRBM_GUI_ACTIVE per XCD)",
-        f"mfma_busy_fraction: {busy / SIMDS / gui_xcd:.3f}  (busy cycles per SIMD over active cycles)",
-        f"clock_mhz_grbm: {gui_xcd / ns * 1e3:.0f}  (GRBM_GUI_ACTIVE per XCD over the dispatch duration)",
-        f"clock_mhz_sq_lower_bound: {sq_busy / SES / ns * 1e3:.0f}  (SQ_BUSY_CYCLES per shader engine; counts "
-        "only cycles with waves present)",
+        f"wave_cycles_per_shader_engine: {wave_cycles:.0f}  (SQ_BUSY_CYCLES over {SES}: cycles with waves present)",
+        f"mfma_busy_fraction: {busy / SIMDS / wave_cycles:.3f}  (matrix-pipe busy cycles per SIMD over the cycles "
+        "with waves present)",
+        f"clock_mhz_lower_bound: {wave_cycles / ns * 1e3:.0f}  (cycles with waves present over the dispatch "
+        "duration; GRBM_GUI_ACTIVE equals GRBM_COUNT here, i.e. it spans the whole counter window, and gives "
+        "no clock)",
         f"lds_bank_conflict_cycles: {conflict:.0f}",
         f"lds_active_cycles: {active:.0f}",
         f"lds_bank_conflicts_per_access: {conflict / max(active - conflict, 1.0):.4f}  (conflict cycles over "
@@ -394,7 +405,7 @@ def summarize_counters(name, digest, csvs, out_path):
         f"traffic_bytes_per_launch: {traffic:.0f}",
         f"algorithmic_bytes_per_launch: {alg:.0f}",
         f"traffic_over_algorithmic: {traffic / alg:.3f}",
-        f"registers: vgpr={vgpr} agpr={agpr} sgpr={sgpr} scratch_bytes={scratch} lds_bytes={lds}",
+        "registers (compiler report of this build): " + " ".join(f"{k}={v}" for k, v in res.items()),
         "# commands, each a run of its own, from /tmp with TMPDIR=/tmp (R = the repository root):",
     ]
     for tag, counters in COUNTER_PASSES.items():
