@@ -247,6 +247,16 @@ int gemm_plan_describe(gemm_plan_t plan, int32_t out[16]);
 int gemm_catalogue(int32_t *cfgs, int32_t max_cfgs);
 
 /*
+ * gemm_catalogue_registers -- for each catalogue entry, the registers per lane (VGPR +
+ * AGPR, in allocation granules) that the planner's occupancy filter assumes a wave of
+ * it holds ("Tiling 策略与内存层次优化", constraint 2: the register budget decides how
+ * many warps stay resident): the largest kernel of its family in the compiler's
+ * resource report of this build.  Writes min(count, max_regs) values to regs (may be
+ * NULL) in catalogue order and returns the count.
+ */
+int gemm_catalogue_registers(int32_t *regs, int32_t max_regs);
+
+/*
  * gemm_autotune -- measure every compiled variant on one problem and keep the
  * fastest ("Tiling 策略与内存层次优化", autotuning section: enumerate the tile
  * configurations, filter out those that break the hardware limits, benchmark each

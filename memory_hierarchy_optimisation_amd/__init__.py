@@ -41,7 +41,7 @@ DESCRIBE_FIELDS = ("kind", "bm", "bn", "bk", "waves_m", "waves_n", "stages", "sp
 EXPORTS = ("gemm_plan", "gemm_plan_config", "gemm_run", "gemm_run_epilogue", "gemm_destroy",
            "gemm_last_error", "gemm_plan_describe", "gemm_catalogue", "gemm_autotune", "gemm_tune_save",
            "gemm_tune_load", "gemm_tune_clear", "gemm_transpose", "gemm_clock_probe",
-           "gemm_run_noalloc")
+           "gemm_run_noalloc", "gemm_catalogue_registers")
 
 
 class Epilogue(ctypes.Structure):
@@ -93,6 +93,8 @@ def _load():
     f32p, i32p = ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_int32)
     lib.gemm_catalogue.argtypes = [i32p, i32]
     lib.gemm_catalogue.restype = i32
+    lib.gemm_catalogue_registers.argtypes = [i32p, i32]
+    lib.gemm_catalogue_registers.restype = i32
     lib.gemm_autotune.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, vp, vp, vp, vp, i32,
                                   i32p, f32p, f32p, i32]
     lib.gemm_autotune.restype = i32
@@ -196,6 +198,14 @@ def gemm_catalogue():
     arr = (ctypes.c_int32 * (8 * n))()
     _lib.gemm_catalogue(arr, n)
     return [tuple(arr[8 * i:8 * i + 8]) for i in range(n)]
+
+
+def gemm_catalogue_registers():
+    """Registers per lane the planner's occupancy filter assumes, per catalogue entry."""
+    n = _lib.gemm_catalogue_registers(None, 0)
+    arr = (ctypes.c_int32 * n)()
+    _lib.gemm_catalogue_registers(arr, n)
+    return list(arr)
 
 
 def gemm_autotune(M, N, K, lda, ldb, ldc, dtype, layout, A, B, C, stream=None, reps=20):

@@ -125,6 +125,8 @@ int elem_bytes(int code);
 int64_t lds_bytes_of(const TileConfig &c, int elem);           // (BM*BK + BK*BN) * elem * stages
 double tile_intensity(int bm, int bn, int elem);                // 2*BM*BN / ((BM+BN)*elem)
 int workgroups_per_cu(const Variant &v, int elem, const Hardware &hw);
+// Registers per lane (VGPR + AGPR) a wave of the variant holds, from the build's report.
+int registers_of(const Variant &v);
 double tail_efficiency(int64_t n_wg, int64_t slots);            // n / (ceil(n/slots) * slots)
 
 // Validate arguments and fill the shape part of a plan.  Returns false and sets *err.

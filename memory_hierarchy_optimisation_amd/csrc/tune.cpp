@@ -123,6 +123,14 @@ int gemm_catalogue(int32_t *cfgs, int32_t max_cfgs) {
   return n;
 }
 
+int gemm_catalogue_registers(int32_t *regs, int32_t max_regs) {
+  int n;
+  const mhg::Variant *cat = mhg::catalogue(&n);
+  if (regs)
+    for (int i = 0; i < n && i < max_regs; ++i) regs[i] = mhg::registers_of(cat[i]);
+  return n;
+}
+
 int gemm_autotune(int64_t M, int64_t N, int64_t K, int64_t lda, int64_t ldb, int64_t ldc, int dtype,
                   int layout, const void *A, const void *B, void *C, void *stream, int32_t reps,
                   int32_t best_cfg[8], float *best_us, float *times_us, int32_t n_times) {

@@ -257,3 +257,44 @@ def test_noalloc_rejects_a_workspace_beyond_its_scratch(tmp_path):
             mh.gemm_run_noalloc(16, 16, 16, 8, 16, 16, mh.GEMM_BF16_F32, 0, 256, 256, 256, stream=0)
     finally:
         mh.gemm_tune_clear()
+
+
+def _report_registers():
+    """Registers per lane of every kernel in the build's resource report, keyed by name:
+    architected VGPRs in 4-register granules, then AGPRs, the total in 8-register
+    allocation granules."""
+    path = os.path.join(ROOT, "_build", "resource_usage.txt")
+    out = {}
+    for line in open(path):
+        name, *kv = line.split()
+        f = dict(x.split("=", 1) for x in kv)
+        v, a = int(f["vgpr"]), int(f["agpr"])
+        out[name] = ((v + 3) // 4 * 4 + a + 7) // 8 * 8
+    return out
+
+
+def _family(cfg):
+    """Pattern of the mangled kernel names that implement a catalogue entry."""
+    kind, bm, bn, bk, _, _, stages, split = cfg
+    if kind == mh.GEMM_KIND_FMA:
+        return rf"fma_gemmILi{bm}E"
+    if kind == mh.GEMM_KIND_SKINNY:
+        return r"skinny_gemm"
+    if bk == 16:
+        return r"mfma32_gemm"
+    if stages == 5:
+        return rf"w8_gemm.*Tile{bm}E"
+    return rf"mfma_gemmINS_\d+Half\w+ELi{bm}ELi{bn}E"
+
+
+def test_occupancy_filter_uses_the_build_report():
+    """The planner's register counts are the largest of each kernel family in the
+    compiler's resource report of this build (not constants)."""
+    report = _report_registers()
+    regs = mh.gemm_catalogue_registers()
+    cat = mh.gemm_catalogue()
+    assert len(regs) == len(cat)
+    for cfg, r in zip(cat, regs):
+        family = [v for k, v in report.items() if re.search(_family(cfg), k)]
+        assert family, cfg
+        assert r == max(family), (cfg, r, max(family))
