@@ -10,18 +10,26 @@
 // is padded by four floats ("CUDA tile", 4, padding against bank conflicts).
 // Out-of-range loads are zero ("CUDA tile", 4: 0 is the identity of the sum) and
 // stores are masked.
+//
+// Global loads: with 16-byte aligned operands whose leading dimensions are multiples
+// of four floats (VEC), each lane loads 16-byte chunks of four consecutive elements
+// along the operand's contiguous dimension, consecutive lanes consecutive chunks (the
+// 128-bit coalesced loads of "Tiling 策略与内存层次优化", step 4); a chunk that
+// crosses an edge of the matrix is loaded element by element.  Otherwise every lane
+// loads single elements, consecutive lanes consecutive addresses.
 #include "device.h"
 
 namespace mhg {
 namespace {
 
-template <int BM, int BN, int BK, int TM, int TN, bool A_COL, bool B_COL>
+template <int BM, int BN, int BK, int TM, int TN, bool A_COL, bool B_COL, bool VEC>
 __global__ void __launch_bounds__((BM / TM) * (BN / TN))
 fma_gemm(LaunchArgs p) {
   constexpr int TX = BN / TN, TY = BM / TM, NT = TX * TY;
   constexpr int AP = BM + 4, BP = BN + 4;
   constexpr int A_PER = BM * BK / NT, B_PER = BK * BN / NT;
   static_assert((BM * BK) % NT == 0 && (BK * BN) % NT == 0, "slab must divide over the lanes");
+  static_assert(!VEC || (A_PER % 4 == 0 && B_PER % 4 == 0), "16-byte chunks must divide over the lanes");
   __shared__ __attribute__((aligned(16))) float As[2][BK][AP];
   __shared__ __attribute__((aligned(16))) float Bs[2][BK][BP];
 
@@ -42,7 +50,69 @@ fma_gemm(LaunchArgs p) {
   };
 
   float ra[A_PER], rb[B_PER];
-  auto load = [&](int k0) {
+  // VEC: chunk e of four consecutive elements of the contiguous dimension -> the
+  // tile position (r, c) of its first element.
+  auto a_chunk = [](int e, int &r, int &c) {
+    if (A_COL) { c = e / (BM / 4); r = 4 * (e % (BM / 4)); } else { r = e / (BK / 4); c = 4 * (e % (BK / 4)); }
+  };
+  auto b_chunk = [](int e, int &r, int &c) {
+    if (B_COL) { r = e / (BK / 4); c = 4 * (e % (BK / 4)); } else { c = e / (BN / 4); r = 4 * (e % (BN / 4)); }
+  };
+  // Four elements starting at src, the first `n` of them inside the matrix.
+  auto load4 = [](const float *src, int n, float *dst) {
+    if (n >= 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(src);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = v[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = e < n ? src[e] : 0.f;
+    }
+  };
+  auto load_vec = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < A_PER / 4; ++i) {
+      int r, c;
+      a_chunk(int(threadIdx.x) + i * NT, r, c);
+      const int64_t gm = m0 + r, gk = k0 + c;
+      // the chunk runs along k (row-major A) or along m (column-major A)
+      const int64_t n = A_COL ? (gk < p.K ? p.M - gm : 0) : (gm < p.M ? p.K - gk : 0);
+      load4(A + (A_COL ? gk * p.lda + gm : gm * p.lda + gk), int(n < 4 ? n : 4), &ra[4 * i]);
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER / 4; ++i) {
+      int r, c;
+      b_chunk(int(threadIdx.x) + i * NT, r, c);
+      const int64_t gn = n0 + r, gk = k0 + c;
+      const int64_t n = B_COL ? (gn < p.N ? p.K - gk : 0) : (gk < p.K ? p.N - gn : 0);
+      load4(B + (B_COL ? gn * p.ldb + gk : gk * p.ldb + gn), int(n < 4 ? n : 4), &rb[4 * i]);
+    }
+  };
+  auto store_vec = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < A_PER / 4; ++i) {
+      int r, c;
+      a_chunk(int(threadIdx.x) + i * NT, r, c);
+      if (A_COL) {
+        *reinterpret_cast<f32x4 *>(&As[buf][c][r]) = f32x4{ra[4 * i], ra[4 * i + 1], ra[4 * i + 2], ra[4 * i + 3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) As[buf][c + e][r] = ra[4 * i + e];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_PER / 4; ++i) {
+      int r, c;
+      b_chunk(int(threadIdx.x) + i * NT, r, c);
+      if (!B_COL) {
+        *reinterpret_cast<f32x4 *>(&Bs[buf][c][r]) = f32x4{rb[4 * i], rb[4 * i + 1], rb[4 * i + 2], rb[4 * i + 3]};
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bs[buf][c + e][r] = rb[4 * i + e];
+      }
+    }
+  };
+  auto load_el = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
       int r, c;
@@ -58,7 +128,7 @@ fma_gemm(LaunchArgs p) {
       rb[i] = (gn < p.N && gk < p.K) ? B[B_COL ? gn * p.ldb + gk : gk * p.ldb + gn] : 0.f;
     }
   };
-  auto store = [&](int buf) {
+  auto store_el = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < A_PER; ++i) {
       int r, c;
@@ -71,6 +141,13 @@ fma_gemm(LaunchArgs p) {
       b_rc(int(threadIdx.x) + i * NT, r, c);
       Bs[buf][c][r] = rb[i];
     }
+  };
+
+  auto load = [&](int k0) {
+    if constexpr (VEC) load_vec(k0); else load_el(k0);
+  };
+  auto store = [&](int buf) {
+    if constexpr (VEC) store_vec(buf); else store_el(buf);
   };
 
   float acc[TM][TN];
@@ -115,17 +192,25 @@ fma_gemm(LaunchArgs p) {
   }
 }
 
-template <int BM, int BN, int BK, int TM, int TN>
-hipError_t launch_fma_tiles(const LaunchArgs &p, hipStream_t s) {
+template <int BM, int BN, int BK, int TM, int TN, bool VEC>
+void launch_fma_layout(const LaunchArgs &p, hipStream_t s) {
   const dim3 grid(unsigned(p.gm) * unsigned(p.gn)), block((BM / TM) * (BN / TN));
   if (!p.a_col && !p.b_col)
-    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, false, false, VEC>), grid, block, 0, s, p);
   else if (!p.a_col && p.b_col)
-    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, false, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, false, true, VEC>), grid, block, 0, s, p);
   else if (p.a_col && !p.b_col)
-    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, true, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, true, false, VEC>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, true, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fma_gemm<BM, BN, BK, TM, TN, true, true, VEC>), grid, block, 0, s, p);
+}
+
+// 16-byte chunks need 16-byte aligned operands with leading dimensions that are
+// multiples of four floats (vec_a, vec_b: checked by gemm_run for fp32 inputs).
+template <int BM, int BN, int BK, int TM, int TN>
+hipError_t launch_fma_tiles(const LaunchArgs &p, hipStream_t s) {
+  if (p.vec_a && p.vec_b) launch_fma_layout<BM, BN, BK, TM, TN, true>(p, s);
+  else launch_fma_layout<BM, BN, BK, TM, TN, false>(p, s);
   return hipGetLastError();
 }
 

@@ -452,3 +452,31 @@ def test_operands_at_high_low_word(cfg, a_col, b_col):
         torch.cuda.empty_cache()
     Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16", a_col, b_col)
     check_exact(got, Cref, "f32", f"cfg={cfg}")
+
+
+def test_clock_probe_reads_a_plausible_clock():
+    """The one-wave clock probe (a measurement helper): shader cycles over a 2 ms window
+    of the 100 MHz real-time counter give a clock between 100 MHz and 3 GHz, and the
+    window it reports is at least the one asked for."""
+    out = torch.zeros(2, dtype=torch.int64, device="cuda")
+    mh.gemm_clock_probe(out.data_ptr(), 200_000)
+    torch.cuda.synchronize()
+    cycles, ticks = (int(v) for v in out.cpu().tolist())
+    assert ticks >= 200_000
+    assert 100.0 <= 100.0 * cycles / ticks <= 3000.0, (cycles, ticks)
+
+
+@pytest.mark.parametrize("a_col,b_col", LAYOUTS)
+def test_fp32_vector_loads_at_edges(a_col, b_col):
+    """The fp32 FMA tiles with 16-byte loads: extents that leave partial 4-element chunks
+    at every edge (ld a multiple of 4, so the vector path is taken), exact integer
+    products, each FMA tile forced."""
+    for cfg in [(1, 32, 32, 32, 4, 1, 2, 1), (1, 64, 64, 16, 4, 1, 2, 1), (1, 128, 128, 16, 4, 1, 2, 1)]:
+        for M, N, K in [(33, 35, 37), (130, 66, 18), (5, 7, 3)]:
+            lda = ((M if a_col else K) + 3) // 4 * 4
+            ldb = ((K if b_col else N) + 3) // 4 * 4
+            As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "f32", a_col, b_col, lda=lda, ldb=ldb, dist="int", seed=M)
+            C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "f32", "f32", a_col, b_col, cfg=cfg)
+            assert (desc["bm"], desc["kind"]) == (cfg[1], 1)
+            check_exact(raw, oracle_ref(As, lda, Bs, ldb, M, N, K, "f32", a_col, b_col), "f32",
+                        f"cfg={cfg} M={M} N={N} K={K}")
