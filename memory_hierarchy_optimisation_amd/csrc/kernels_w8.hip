@@ -370,12 +370,16 @@ struct W8Gemm {
                                              in ? uint32_t((int64_t(r) * p.ldc + 8 * c) * 2) : kOut, 0, 0, 0);
   }
 
-  // Memory phase for slab t: read all of the wave's fragments of slab t, then request
-  // its loads of slab t+4 (into the slot of slab t-1, which every wave has finished
-  // reading: the last reader ended its phase with every read complete).  The requests
-  // come after the reads: issued among them they kept the reads apart (about 20 cycles
-  // each); after them they overlap the wait for the last reads (4096^3: 1250 -> 1280
-  // TFLOP/s).  PAST: slab t + 4 lies past K (the last four slabs of the 256 x 256 loop).
+  // Memory phase for slab t: read all of the wave's fragments of slab t, then (256 x 256)
+  // request its loads of slab t+4 (into the slot of slab t-1, which every wave has
+  // finished reading: the last reader ended its phase with every read complete).  The
+  // requests come after the reads: issued among them they kept the reads apart (about
+  // 20 cycles each); after them they overlap the wait for the last reads (4096^3: 1250
+  // -> 1280 TFLOP/s).  PAST: slab t + 4 lies past K (the last four slabs of the
+  // 256 x 256 loop).  When the groups take alternate slabs (128 x 128, 64 x 64) the
+  // memory phase is the longer one of the pair (its reads and eight requests against
+  // 16 or 8 matrix instructions), so the requests go into the compute phase instead,
+  // between the matrix instructions (compute).
   template <int S>
   __device__ __forceinline__ void mem_steps(uint32_t sa, uint32_t slot) {
     if constexpr (S < STEPS) { reads_from<S, 0>(sa, slot); mem_steps<S + 1>(sa, slot); }
@@ -411,29 +415,43 @@ struct W8Gemm {
   __device__ __forceinline__ void mem(int t) {
     fa_cur = fa_off[0];
     mem_steps<0>(slot_addr(t), slot_addr(t));
-    const int k0 = (t + AHEAD) * BK;
-    const uint32_t dst = slot_addr(t + AHEAD);
+    if constexpr (!ALT) {             // ALT: requested by compute(t)
+      const int k0 = (t + AHEAD) * BK;
+      const uint32_t dst = slot_addr(t + AHEAD);
 #pragma unroll
-    for (int j = 0; j < LOADS; ++j) {
-      if constexpr (ALT) {
-        ld.issue(k0, kdim - k0, dst, gw, j);
-        ld2.issue(k0, kdim - k0, dst, gw, j);
-      } else if constexpr (PAST) {
-        load(t + AHEAD, dst, j);
-      } else {
-        ld.issue(k0, kdim - k0, dst, gw, j);
+      for (int j = 0; j < LOADS; ++j) {
+        if constexpr (PAST) load(t + AHEAD, dst, j);
+        else ld.issue(k0, kdim - k0, dst, gw, j);
+        MHG_ORDER();
       }
-      MHG_ORDER();
     }
     wait_lgkm<0>();
     MHG_ORDER();
   }
   // Compute phase: the wave's STEPS FM FN matrix instructions of a slab, back to back.
-  __device__ __forceinline__ void compute() {
+  // Groups on alternate slabs (ALT) request both operands of their slab t + 4 here, one
+  // request after every few matrix instructions: slab t + 4's slot held slab t - 1,
+  // which the other group finished reading two phases ago, and the compute phase has
+  // room for the requests that the memory phase has not (2048^3 NT 26.1 -> 25.6 us,
+  // 1024^3 9.3-9.7 -> 8.8-8.9 us, 1000^3 10.1-10.3 -> 9.7 us on one box).
+  __device__ __forceinline__ void compute(int t = 0) {
+    constexpr int NMF = STEPS * FM * FN, EVERY = NMF / (2 * LOADS);
+    static_assert(!ALT || (EVERY >= 1 && NMF % (2 * LOADS) == 0), "requests spread over the matrix instructions");
+    const int k0 = (t + AHEAD) * BK;
+    const uint32_t dst = slot_addr(t + AHEAD);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
 #pragma unroll
       for (int m = 0; m < FM * FN; ++m) {
+        if constexpr (ALT) {
+          const int n = s * FM * FN + m;
+          if (n % EVERY == EVERY - 1) {
+            const int q = n / EVERY;
+            if (q < LOADS) ld.issue(k0, kdim - k0, dst, gw, q);
+            else ld2.issue(k0, kdim - k0, dst, gw, q - LOADS);
+            MHG_ORDER();
+          }
+        }
         const int i = m / FN, j = m % FN;
         const u32x4 a = {fa[s][i][0].x, fa[s][i][0].y, fa[s][i][1].x, fa[s][i][1].y};
         const u32x4 b = {fb[s][j][0].x, fb[s][j][0].y, fb[s][j][1].x, fb[s][j][1].y};
@@ -572,7 +590,7 @@ struct W8Gemm {
     } else {
       // Group g reads, requests and multiplies the slabs t = g mod 2: slab t is read in
       // phase t and multiplied in phase t + 1, and slab t + 4 (the group's own) is
-      // requested while slab t is read.  Slab t + 2 must be in LDS when phase t + 2
+      // requested while slab t is multiplied.  Slab t + 2 must be in LDS when phase t + 2
       // starts, so after multiplying a wave waits until only its slab t + 4 (8 loads) is
       // in flight; slabs past K load zeros, so both groups run the same trip count.
       issue_all(int(grp));
@@ -586,7 +604,7 @@ struct W8Gemm {
         wait_vm<4 * LOADS>();
         barrier();
         MHG_ORDER();
-        compute();
+        compute(2 * u + int(grp));
         wait_vm<2 * LOADS>();
         barrier();
         MHG_ORDER();
