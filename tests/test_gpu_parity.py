@@ -16,7 +16,7 @@ import torch
 import memory_hierarchy_optimisation_amd as mh
 import oracle
 import synth
-from gemm_cases import check_exact, check_tolerance, oracle_ref, run_gpu
+from gemm_cases import SENTINEL16, SENTINEL32, check_exact, check_tolerance, oracle_ref, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -215,6 +215,36 @@ def test_eight_wave_kernels_unaligned_c(cfg, out_t):
     for offset_c, ldc in ((0, N), (1, N), (0, N + 4)):
         C, raw, desc = run_gpu(As, lda, Bs, ldb, M, N, K, "bf16", out_t, ldc=ldc, cfg=cfg, offset_c=offset_c)
         check_tolerance(C, Cref, out_t, f"offset_c={offset_c} ldc={ldc}")
+
+
+@pytest.mark.parametrize("out_t,ldc", [("f32", 4194304 - 64), ("f32", 4194304 + 8), ("bf16", 8388608 + 8)],
+                         ids=["f32-below", "f32-above", "bf16-above"])
+def test_staged_stores_long_rows_of_c(out_t, ldc):
+    """The 256 x 256 tile's staged stores go through a buffer resource based at the
+    wave's block of C, whose offsets must stay below 2^31 bytes; a C whose 128 rows of a
+    block span more than that takes streaming global stores instead.  Just below the
+    limit (offsets near 2^31) and above it (4.4 GB of C), both output types; the padding
+    columns, checked on the device, must keep their sentinel."""
+    M, N, K = 264, 264, 136
+    As, lda, Bs, ldb, _, _ = synth.operands(M, N, K, "bf16", seed=31)
+    Cref = oracle_ref(As, lda, Bs, ldb, M, N, K, "bf16")
+    eb = 4 if out_t == "f32" else 2
+    print(f"[long rows] out={out_t} ldc={ldc} C bytes={M * ldc * eb}", flush=True)
+    sent = SENTINEL32 if out_t == "f32" else SENTINEL16
+    cbuf = torch.full((M, ldc), sent, dtype=torch.int32 if out_t == "f32" else torch.int16, device="cuda")
+    A, B = As.cuda(), Bs.cuda()
+    plan = mh.gemm_plan_config(M, N, K, lda, ldb, ldc, mh.DTYPE_OF[("bf16", out_t)], 0, W8_256)
+    try:
+        mh.gemm_run(plan, A, B, cbuf)
+        torch.cuda.synchronize()
+    finally:
+        mh.gemm_destroy(plan)
+    assert not bool((cbuf[:, N:] != sent).any()), "write into the padding columns of C"
+    body = cbuf[:, :N].cpu().numpy()
+    del cbuf
+    torch.cuda.empty_cache()
+    vals = body.view(np.float32).astype(np.float64) if out_t == "f32" else oracle.decode(body.view(np.uint16), out_t)
+    check_tolerance(vals, Cref, out_t, f"ldc={ldc}")
 
 
 def SKINNY(split):
