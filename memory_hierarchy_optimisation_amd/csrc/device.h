@@ -36,18 +36,6 @@ __device__ __forceinline__ f32x4 mfma16(HalfF16, u32x4 a, u32x4 b, f32x4 acc) {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// One 32x32x16 matrix multiply-accumulate on a wave: acc += A(32x16) * B(16x32).
-// Lane l holds A row (l % 32), k = 8*(l/32) .. +7 and B column (l % 32) over the same
-// k; accumulator element r holds row 8*(r/4) + 4*(l/32) + r%4 of column l % 32.
-__device__ __forceinline__ f32x16 mfma32(HalfBF16, u32x4 a, u32x4 b, f32x16 acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                 __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
-}
-__device__ __forceinline__ f32x16 mfma32(HalfF16, u32x4 a, u32x4 b, f32x16 acc) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
-                                                __builtin_bit_cast(f16x8, b), acc, 0, 0, 0);
-}
-
 // LDS transpose read of four 16-bit elements.  Within each group of 16 lanes, lane t
 // receives element (t & 3) of the 8-byte rows addressed by lanes 4q + (t >> 2),
 // q = 0..3: a 4 x 16 block of a row-major tile comes back column by column.

@@ -24,9 +24,13 @@
 //   * K slabs in a ring of five 32 KiB LDS slots (constraint 1 of the same page with
 //     stages = 5), requested four slabs ahead with 16-byte LDS-destination buffer
 //     loads, the gfx950 counterpart of cp.async (cp.async section);
-//   * eight waves, two per SIMD, each with a 32 x 32 accumulator tile per
-//     v_mfma_f32_32x32x16_{bf16,f16} ("寄存器Tiling", 1.3: the register budget trades
-//     tile size for resident waves; 128 or 64 fp32 accumulators a lane).
+//   * eight waves, two per SIMD, each with a register tile of 16 x 16 accumulator blocks
+//     of v_mfma_f32_16x16x32_{bf16,f16} ("寄存器Tiling", 1.3: the register budget trades
+//     tile size for resident waves; 128, 64 or 16 fp32 accumulators a lane).  The
+//     16 x 16 instruction does the same work per cycle as the 32 x 32 one but moves half
+//     the accumulator bytes per multiply-add; on random data the chip, at its power
+//     limit, holds a higher clock with it (a stream of either instruction alone: 2.03 vs
+//     1.76 GHz; these kernels at 4096^3: 1.74-1.77 vs 1.51-1.63 GHz).
 // Ping-pong: the waves form two groups, one wave of each per SIMD.  Block barriers
 // cut time into phases; in each phase one group runs the matrix instructions of a
 // slab back to back, with no memory instruction among them, while the other group
@@ -71,8 +75,9 @@ constexpr int LOADS = OP_BYTES / (GROUP * 64 * 16);   // 16-byte loads per lane 
 constexpr int AHEAD = 4;                        // slab t+4 is requested while slab t is read
 constexpr uint32_t kOut = 0x80000000u;          // beyond every buffer range: loads zeros
 
-// The tile shapes.  FM x FN accumulators of 32 x 32 per wave; KSPLIT = 2: the groups
-// take alternate slabs (halves of K) instead of halves of the rows.
+// The tile shapes.  A wave's block of C is 32 FM x 32 FN (2 FM x 2 FN accumulators of
+// 16 x 16); KSPLIT = 2: the groups take alternate slabs (halves of K) instead of halves
+// of the rows.
 // PAIRA: with A row-major and B column-major, the 256 x 256 tile brings A in pairs of
 // slabs, whole 128-byte rows (see the pair ring below).
 struct Tile256 { static constexpr int BM = 256, BN = 256, BK = 32, FM = 4, FN = 2, KSPLIT = 1; static constexpr bool PAIRA = true; };
@@ -89,20 +94,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void *base) {
 // LDS layouts of one operand's slab (byte offsets within its 16 KiB), for a tile side
 // of R rows (m or n) and slabs BK deep:
 //   K-contiguous: row r (0..R-1) of BK/8 16-byte k-chunks; chunk c at
-//     r * 2BK + 16 (c ^ kswz(r)), kswz(r) = (r >> 2) & 3 for 4 chunks a row,
-//     (r >> 1) & 7 for 8, r & 15 for 16.  Sixteen consecutive rows read at one chunk (a
-//     fragment read, 16 lanes an LDS cycle) land on 16 distinct 16-byte bank groups.
+//     r * 2BK + 16 (c ^ kswz(r)).  A fragment read has lane l read chunk l / 16 of row
+//     l % 16 (plus the block's and step's offsets).  The LDS serves a 16-byte read in four
+//     passes of 16 lanes: the four-lane quads of one half-wave (lane bit 5) whose quad
+//     index has the same parity (bits 2 ^ 3 ^ 4), e.g. lanes 0-3, 12-15, 20-23 and 24-27
+//     (measured on the MI355X with the LDS conflict counter: one lane pair per dispatch
+//     at the same banks, the rest broadcasting).  In a pass, row bits 0 and 1 and two of
+//     bits 2, 3 and 4 vary; kswz puts its 16 reads on distinct 16-byte bank groups.  With
+//     4 chunks a row (4 rows per 256 bytes of banks) kswz(r) = 2 ((r >> 3) & 1): then
+//     chunk bit 0 follows bit 2 ^ 3 ^ 4 ^ parity and chunk bit 1 bit 3, which separate
+//     the four (bit 2, bit 3) choices (the plain (r >> 2) & 3 left only bit 3 and
+//     conflicted two-way); (r >> 1) & 7 for 8 chunks and r & 15 for 16 separate them
+//     already.
 //   M/N-contiguous: k-row k (0..BK-1) of R/8 chunks of 8 m/n-values; chunk c at
-//     k * 2R + 16 (c ^ mswz(k)).  A transpose read touches four consecutive k-rows, 64
-//     bytes each, in one LDS cycle; mswz(k) = 4 (k & 3) moves 512- or 256-byte k-rows
-//     to four distinct quarters of the banks, 4 ((k >> 1) & 1) the 128-byte k-rows of
-//     the 64-wide tile (rows k and k+1 already sit half the banks apart).
+//     k * 2R + 16 (c ^ mswz(k)).  The 32 lanes of a transpose read served together read
+//     32 bytes of the same columns in each of four consecutive k-rows k0 + q and of four
+//     more, k0 + 8 + q (their fragments' k differ by 8).  mswz(k) = 4 (k & 3) moves 512-
+//     or 256-byte k-rows to four distinct quarters of the banks (4 ((k >> 1) & 1) the
+//     128-byte k-rows of the 64-wide tile, whose rows k and k+1 already sit half the
+//     banks apart), and the term 2 ((k >> 3) & 1) puts the second four k-rows in the
+//     other half of each quarter.
 template <int BK>
 __device__ __forceinline__ constexpr int kswz(int r) {
-  return BK == 32 ? (r >> 2) & 3 : BK == 64 ? (r >> 1) & 7 : r & 15;
+  return BK == 32 ? 2 * ((r >> 3) & 1) : BK == 64 ? (r >> 1) & 7 : r & 15;
 }
 template <int R>
-__device__ __forceinline__ constexpr int mswz(int k) { return R >= 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+__device__ __forceinline__ constexpr int mswz(int k) {
+  return (R >= 128 ? 4 * (k & 3) : 4 * ((k >> 1) & 1)) ^ (2 * ((k >> 3) & 1));
+}
 template <int BK>
 __device__ __forceinline__ uint32_t kc_off(int r, int c) { return uint32_t(r * 2 * BK + 16 * (c ^ kswz<BK>(r))); }
 template <int R>
@@ -203,27 +222,28 @@ struct PairLoader {
   }
 };
 
-// Fragment addressing.  A 32 x 16 fragment (32 rows of m or n, 16 k) for
-// v_mfma_f32_32x32x16: lane l holds row l % 32, k = 8 (l / 32) .. +7 of the 16-deep
+// Fragment addressing.  A 16 x 32 fragment (16 rows of m or n, 32 k) for
+// v_mfma_f32_16x16x32: lane l holds row l % 16, k = 8 (l / 16) .. +7 of the 32-deep
 // step s.
-//   K-contiguous: one 16-byte read at kc_off(32 b + l % 32, 2 s + l / 32).  The swizzle
-//     term depends on the lane only (32 b leaves bits 0..4 of the row alone), and
-//     (2 s + l / 32) ^ x = 2 s ^ (l / 32 ^ x) since 2 s has no bit in common with l / 32,
-//     so step s is an XOR of 32 s on the lane's offset (below the row's 2BK bytes) and
-//     block b a constant 32 b * 2BK.
-//   M/N-contiguous: two transpose reads (e = 0, 1) for k = 8 (l / 32) + 4 e .. +3.  In
+//   K-contiguous: one 16-byte read at kc_off(16 b + l % 16, 4 s + l / 16).  The swizzle
+//     term depends on the row's bits 0..3 only, i.e. on the lane (16 b leaves them
+//     alone), and (4 s + l / 16) ^ x = 4 s ^ (l / 16 ^ x) since 4 s has no bit in common
+//     with l / 16, so step s is an XOR of 64 s on the lane's offset (below the row's 2BK
+//     bytes: only slabs 64 or more deep have a second step) and block b a constant
+//     16 b * 2BK.
+//   M/N-contiguous: two transpose reads (e = 0, 1) for k = 8 (l / 16) + 4 e .. +3.  In
 //     each 16-lane group g = l / 16, lane 4 q + u addresses the 8 bytes of k-row
-//     16 s + 8 (g / 2) + 4 e + q, columns 32 b + 16 (g % 2) + 4 u .. +3, and lane t then
-//     receives column 32 b + 16 (g % 2) + t of those four k-rows; step s adds 16 s * 2R
-//     and e adds 4 * 2R to the lane's offset for step 0, e = 0 (mswz depends on k's low
-//     two bits only, which are q's).
+//     32 s + 8 g + 4 e + q, columns 16 b + 4 u .. +3, and lane t then receives column
+//     16 b + t of those four k-rows; step s adds 32 s * 2R and e adds 4 * 2R to the
+//     lane's offset for step 0, e = 0 (mswz depends on k's bits 0, 1 and 3, which are
+//     q's and g's).
 template <int BK>
-__device__ __forceinline__ uint32_t kc_lane(int lane) { return kc_off<BK>(lane & 31, lane >> 5); }
+__device__ __forceinline__ uint32_t kc_lane(int lane) { return kc_off<BK>(lane & 15, lane >> 4); }
 template <int R>
 __device__ __forceinline__ uint32_t mn_lane(int lane, int b) {
   const int g = lane >> 4, t = lane & 15, q = t >> 2, u = t & 3;
-  const int k = 8 * (g >> 1) + q;
-  const int c = 4 * b + 2 * (g & 1) + (u >> 1);
+  const int k = 8 * g + q;
+  const int c = 2 * b + (u >> 1);
   return mn_off<R>(k, c) + 8 * (u & 1);
 }
 
@@ -260,8 +280,9 @@ template <class H, bool A_KC, bool B_KC, class TL, bool PRIOR>
 struct W8Gemm {
   static constexpr int BM = TL::BM, BN = TL::BN, BK = TL::BK, FM = TL::FM, FN = TL::FN;
   static constexpr bool ALT = TL::KSPLIT == 2;           // groups take alternate slabs
-  static constexpr int STEPS = BK / 16;                  // 16-deep steps of a slab
+  static constexpr int STEPS = BK / 32;                  // 32-deep steps of a slab
   static constexpr int WTM = 32 * FM, WTN = 32 * FN;      // a wave's block of C
+  static constexpr int MB = 2 * FM, NBL = 2 * FN;         // its 16 x 16 blocks
   static_assert(BM * BK * 2 == OP_BYTES && BN * BK * 2 == OP_BYTES, "slab size");
   static_assert(!PRIOR || (!ALT && FM == 4 && FN == 2), "prior C through LDS: 256 x 256 tile only");
   // PA: A (row-major) in a ring of three 32 KiB pair slots, each the tile's 256 rows of
@@ -287,44 +308,40 @@ struct W8Gemm {
   PairLoader lp;              // PA: group 0's loader of A
   uint32_t fa_cur;            // fa_off[0] with the slab's half of an A pair applied (PA)
   // Lane offsets of the fragment reads within an operand slab (step 0), the wave's
-  // block offset included: K-contiguous operands use [0] (step s is [0] ^ 32 s, block i
-  // adds 64 BK i); M/N-contiguous ones one per block (step s adds 16 s k-rows).
-  uint32_t fa_off[FM], fb_off[FN];
-  f32x16 acc[FM][FN];
+  // block offset included: K-contiguous operands use [0] (step s is [0] ^ 64 s, block i
+  // adds 32 BK i); M/N-contiguous ones one per block (step s adds 32 s k-rows).
+  uint32_t fa_off[MB], fb_off[NBL];
+  f32x4 acc[MB][NBL];
   // The fragments of one slab, [step][block][half] (k 0..3 and 4..7 of the lane's
   // eight): a 16-byte read fills both halves, a transpose read one.
-  u32x2 fa[STEPS][FM][2], fb[STEPS][FN][2];
+  u32x2 fa[STEPS][MB][2], fb[STEPS][NBL][2];
 
   static constexpr int NA = A_KC ? 1 : 2, NB = B_KC ? 1 : 2;
-  static constexpr int T = FN * NB + FM * NA;            // LDS reads per step
+  static constexpr int T = NBL * NB + MB * NA;           // LDS reads per step
 
   __device__ __forceinline__ W8Gemm(const LaunchArgs &p_) : p(p_) {}
 
-  // Read k of a step, in the order the step's matrix instructions need them (B block 0,
-  // A block 0, B block 1, A blocks 1 ..); a fragment is one read if K-contiguous, two
-  // if M/N-contiguous.  Returns the fragment (0 .. FM-1: A block, FM ..: B block).
-  static constexpr int read_frag(int k) {
-    return k < NB ? FM : k < NB + NA ? 0 : k < 2 * NB + NA ? FM + 1 : 1 + (k - 2 * NB - NA) / NA;
-  }
-  static constexpr int read_half(int k) {
-    return k < NB ? k : k < NB + NA ? k - NB : k < 2 * NB + NA ? k - NB - NA : (k - 2 * NB - NA) % NA;
-  }
-  // Read k of the wave's step S (0 or 1) from the slab whose A area is `slot`.
+  // Read k of a step: the B blocks, then the A blocks; a fragment is one read if
+  // K-contiguous, two if M/N-contiguous.  Returns the fragment (0 .. MB-1: A block,
+  // MB ..: B block).
+  static constexpr int read_frag(int k) { return k < NBL * NB ? MB + k / NB : (k - NBL * NB) / NA; }
+  static constexpr int read_half(int k) { return k < NBL * NB ? k % NB : (k - NBL * NB) % NA; }
+  // Read k of the wave's step S from the slab whose A area is `slot`.
   template <int S, int K>
   __device__ __forceinline__ void read(uint32_t sa, uint32_t slot) {
     constexpr int f = read_frag(K), h = read_half(K);
-    if constexpr (f < FM) {
+    if constexpr (f < MB) {
       if constexpr (A_KC) {
-        ds_b128<64 * BKA * f>(*reinterpret_cast<u32x4 *>(&fa[S][f][0]), sa + (fa_cur ^ uint32_t(32 * S)));
+        ds_b128<32 * BKA * f>(*reinterpret_cast<u32x4 *>(&fa[S][f][0]), sa + (fa_cur ^ uint32_t(64 * S)));
       } else {
-        ds_tr<16 * S * 2 * BM + 4 * 2 * BM * h>(fa[S][f][h], sa + fa_off[f]);
+        ds_tr<32 * S * 2 * BM + 4 * 2 * BM * h>(fa[S][f][h], sa + fa_off[f]);
       }
     } else {
-      constexpr int j = f - FM;
+      constexpr int j = f - MB;
       if constexpr (B_KC) {
-        ds_b128<OP_BYTES + 64 * BK * j>(*reinterpret_cast<u32x4 *>(&fb[S][j][0]), slot + (fb_off[0] ^ uint32_t(32 * S)));
+        ds_b128<OP_BYTES + 32 * BK * j>(*reinterpret_cast<u32x4 *>(&fb[S][j][0]), slot + (fb_off[0] ^ uint32_t(64 * S)));
       } else {
-        ds_tr<OP_BYTES + 16 * S * 2 * BN + 4 * 2 * BN * h>(fb[S][j][h], slot + fb_off[j]);
+        ds_tr<OP_BYTES + 32 * S * 2 * BN + 4 * 2 * BN * h>(fb[S][j][h], slot + fb_off[j]);
       }
     }
   }
@@ -438,16 +455,16 @@ struct W8Gemm {
   // room for the requests that the memory phase has not (2048^3 NT 26.1 -> 25.6 us,
   // 1024^3 9.3-9.7 -> 8.8-8.9 us, 1000^3 10.1-10.3 -> 9.7 us on one box).
   __device__ __forceinline__ void compute(int t = 0) {
-    constexpr int NMF = STEPS * FM * FN, EVERY = NMF / (2 * LOADS);
+    constexpr int NMF = STEPS * MB * NBL, EVERY = NMF / (2 * LOADS);
     static_assert(!ALT || (EVERY >= 1 && NMF % (2 * LOADS) == 0), "requests spread over the matrix instructions");
     const int k0 = (t + AHEAD) * BK;
     const uint32_t dst = slot_addr(t + AHEAD);
 #pragma unroll
     for (int s = 0; s < STEPS; ++s)
 #pragma unroll
-      for (int m = 0; m < FM * FN; ++m) {
+      for (int m = 0; m < MB * NBL; ++m) {
         if constexpr (ALT) {
-          const int n = s * FM * FN + m;
+          const int n = s * MB * NBL + m;
           if (n % EVERY == EVERY - 1) {
             const int q = n / EVERY;
             if (q < LOADS) ld.issue(k0, kdim - k0, dst, gw, q);
@@ -455,10 +472,10 @@ struct W8Gemm {
             MHG_ORDER();
           }
         }
-        const int i = m / FN, j = m % FN;
+        const int i = m / NBL, j = m % NBL;
         const u32x4 a = {fa[s][i][0].x, fa[s][i][0].y, fa[s][i][1].x, fa[s][i][1].y};
         const u32x4 b = {fb[s][j][0].x, fb[s][j][0].y, fb[s][j][1].x, fb[s][j][1].y};
-        acc[i][j] = mfma32(H{}, b, a, acc[i][j]);
+        acc[i][j] = mfma16(H{}, b, a, acc[i][j]);
         MHG_ORDER();
       }
   }
@@ -497,21 +514,21 @@ struct W8Gemm {
       ld2.init<B_KC, BN, BK>(B, p.ldb, n0, p.N, gw, lane, OP_BYTES);
     }
     if (A_KC) {
-      fa_off[0] = kc_lane<BKA>(lane) + 64 * BKA * FM * wm;
+      fa_off[0] = kc_lane<BKA>(lane) + 2 * BKA * WTM * wm;
     } else {
 #pragma unroll
-      for (int i = 0; i < FM; ++i) fa_off[i] = mn_lane<BM>(lane, FM * wm + i);
+      for (int i = 0; i < MB; ++i) fa_off[i] = mn_lane<BM>(lane, MB * wm + i);
     }
     if (B_KC) {
-      fb_off[0] = kc_lane<BK>(lane) + 64 * BK * FN * wn;
+      fb_off[0] = kc_lane<BK>(lane) + 2 * BK * WTN * wn;
     } else {
 #pragma unroll
-      for (int j = 0; j < FN; ++j) fb_off[j] = mn_lane<BN>(lane, FN * wn + j);
+      for (int j = 0; j < NBL; ++j) fb_off[j] = mn_lane<BN>(lane, NBL * wn + j);
     }
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = f32x16{};
+      for (int j = 0; j < NBL; ++j) acc[i][j] = f32x4{};
     kdim = int(p.K);
     const int KT = (kdim + BK - 1) / BK;
 
@@ -623,41 +640,34 @@ struct W8Gemm {
     if (TL::KSPLIT == 2) {
       // Group 1 hands its partial sums to its partner wave of group 0 (same block of C)
       // through LDS, lane-major so that neither side has bank conflicts.
-      const uint32_t handoff = lds0 + gw * (FM * FN * 16 * 64 * 4);
+      const uint32_t handoff = lds0 + gw * (MB * NBL * 64 * 16);
       if (grp == 1) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-              *reinterpret_cast<MHG_LDS f32x4 *>(size_t(handoff + (((i * FN + j) * 4 + q) * 64 + lane) * 16)) = v;
-            }
+          for (int j = 0; j < NBL; ++j)
+            *reinterpret_cast<MHG_LDS f32x4 *>(size_t(handoff + ((i * NBL + j) * 64 + lane) * 16)) = acc[i][j];
       }
       barrier();
       if (grp == 1) return;
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v = *reinterpret_cast<const MHG_LDS f32x4 *>(
-                size_t(handoff + (((i * FN + j) * 4 + q) * 64 + lane) * 16));
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] += v[e];
-          }
+        for (int j = 0; j < NBL; ++j)
+          acc[i][j] += *reinterpret_cast<const MHG_LDS f32x4 *>(size_t(handoff + ((i * NBL + j) * 64 + lane) * 16));
     }
     // Staging areas: past the hand-off areas (4 x 16 KiB) when the groups split K.
     epilogue(lane, TL::KSPLIT == 2 ? lds0 + 65536 + gw * 16384 : lds0 + wave * 16384);
   }
 
-  // acc[i][j] holds the transposed 32 x 32 block: element r of lane l is
-  // C[row WTM wm + 32 i + l % 32][col WTN wn + 32 j + 8 (r / 4) + 4 (l / 32) + r % 4] of
-  // the tile.  A lane's four consecutive columns are a 16-byte piece of one row, and a
-  // store instruction would touch 32 rows; staged through the wave's 16 KiB of LDS at
-  // `region` instead, every store writes whole 64-column row segments of C.
+  // acc[i][j] holds the transposed 16 x 16 block (B's fragment is the instruction's
+  // first operand): element e of lane l is C[row WTM wm + 16 i + l % 16][col WTN wn +
+  // 16 j + 4 (l / 16) + e] of the tile.  A lane's four consecutive columns are a piece
+  // of one row (16 bytes of fp32), and a store instruction would touch 16 rows; staged
+  // through the wave's 16 KiB of LDS at `region` instead, every store writes whole
+  // 64-column row segments of C.
+  static __device__ __forceinline__ int piece_row(int i, int lane) { return 16 * i + (lane & 15); }
+  static __device__ __forceinline__ int piece_col(int j, int lane) { return 16 * j + 4 * (lane >> 4); }
   __device__ __forceinline__ void epilogue(int lane, uint32_t region) {
     const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
     const int ob = p.out_code == E_F32 ? 4 : 2;
@@ -677,42 +687,30 @@ struct W8Gemm {
       // are requested before its first store: the compiler may not move a load above
       // a store that might alias it.
       if (p.epi && p.beta == 0.0f && p.out_code != E_F32) {
-        const int64_t colL = colW + 4 * (lane >> 5);
-        f32x4 b[FN][4];
+        f32x4 b[NBL];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < NBL; ++j) {
+          const int64_t col = colW + piece_col(j, lane);
+          b[j] = col < p.N ? bias4(p, col, p.N - col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t col = colL + 32 * j + 8 * q;
-            b[j][q] = col < p.N ? bias4(p, col, p.N - col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-          }
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-              const f32x4 f = epilogue4pb(p, v, f32x4{0.0f, 0.0f, 0.0f, 0.0f}, b[j][q], 4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) acc[i][j][4 * q + e] = f[e];
-            }
+          for (int j = 0; j < NBL; ++j) acc[i][j] = epilogue4pb(p, acc[i][j], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, b[j], 4);
       }
       if (p.out_code == E_F32 || (p.epi && p.beta != 0.0f)) {
-        // 64 rows of 256 bytes a pass; chunk c of row r at 16 (c ^ (r % 16)): sixteen
-        // rows written at one chunk hit 16 bank groups
+        // 64 rows of 256 bytes a pass; chunk c of row r at 16 (c ^ (r % 16)), which keeps
+        // the 16-byte writes (16 rows at 4 chunks) and the read-back (4 rows at 16
+        // chunks) free of bank conflicts
 #pragma unroll
         for (int pass = 0; pass < FM / 2; ++pass) {
 #pragma unroll
-          for (int i2 = 0; i2 < 2; ++i2)
+          for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const int i = 2 * pass + i2, r = 32 * i2 + (lane & 31), c = 8 * j + 2 * q + (lane >> 5);
-                const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-                *reinterpret_cast<MHG_LDS f32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15)))) = v;
-              }
+            for (int j = 0; j < NBL; ++j) {
+              const int r = piece_row(i4, lane), c = piece_col(j, lane) >> 2;
+              *reinterpret_cast<MHG_LDS f32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15)))) = acc[4 * pass + i4][j];
+            }
           if (!p.epi) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
@@ -743,22 +741,21 @@ struct W8Gemm {
           }
         }
       } else {
-        // 128 bytes a row; chunk c of row r at 16 (c ^ ((r / 2) % 8))
+        // 128 bytes a row; chunk c of row r at 16 (c ^ ((r / 2) % 8)); a lane's piece is
+        // half a chunk
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < MB; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
+          for (int j = 0; j < NBL; ++j) {
+            const int r = piece_row(i, lane), col = piece_col(j, lane);
+            uint16_t h[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int r = 32 * i + (lane & 31), c = 4 * j + q;
-              uint16_t h[4];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                h[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][4 * q + e])
-                                           : __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][4 * q + e]);
-              const u32x2 v = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-              *reinterpret_cast<MHG_LDS u32x2 *>(size_t(region + r * 128 + 16 * (c ^ ((r >> 1) & 7)) + 8 * (lane >> 5))) = v;
-            }
+            for (int e = 0; e < 4; ++e)
+              h[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e])
+                                         : __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][e]);
+            const u32x2 v = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+            *reinterpret_cast<MHG_LDS u32x2 *>(size_t(region + r * 128 + 16 * ((col >> 3) ^ ((r >> 1) & 7)) + 2 * (col & 7))) = v;
+          }
 #pragma unroll
         for (int k = 0; k < WTM / 8; ++k) {
           const int r = 8 * k + (lane >> 3), c = lane & 7;
@@ -768,37 +765,28 @@ struct W8Gemm {
       }
       return;
     }
-    const int64_t row0 = rowW + (lane & 31);
-    const int64_t colL = colW + 4 * (lane >> 5);
     const bool c_vec = p.c_vec != 0;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int64_t row = row0 + 32 * i;
+    for (int i = 0; i < MB; ++i) {
+      const int64_t row = rowW + piece_row(i, lane);
       if (row >= p.M) continue;
       // With an epilogue, the row block's bias and prior values are requested before its
       // first store (a load may not move above a store that might alias it).
-      f32x4 ep[FN][4];
+      f32x4 ep[NBL];
       if (p.epi) {
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t col = colL + 32 * j + 8 * q;
-            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-            ep[j][q] = col < p.N ? epilogue4(p, v, row, col, p.N - col) : v;
-          }
+        for (int j = 0; j < NBL; ++j) {
+          const int64_t col = colW + piece_col(j, lane);
+          ep[j] = col < p.N ? epilogue4(p, acc[i][j], row, col, p.N - col) : acc[i][j];
+        }
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t col = colL + 32 * j + 8 * q;
-          const int64_t n_in = p.N - col;
-          if (n_in <= 0) continue;
-          const f32x4 v = p.epi ? ep[j][q]
-                                : f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          store_out4(p.C, row * p.ldc + col, v, p.out_code, c_vec && n_in >= 4, int(n_in));
-        }
+      for (int j = 0; j < NBL; ++j) {
+        const int64_t col = colW + piece_col(j, lane);
+        const int64_t n_in = p.N - col;
+        if (n_in <= 0) continue;
+        store_out4(p.C, row * p.ldc + col, p.epi ? ep[j] : acc[i][j], p.out_code, c_vec && n_in >= 4, int(n_in));
+      }
     }
   }
 
@@ -813,39 +801,33 @@ struct W8Gemm {
   }
   __device__ __forceinline__ void epilogue_prior(int lane) {
     const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
-    const int colL = wn * WTN + 4 * (lane >> 5);          // tile column of the lane's first piece
-    f32x4 b[FN][4];
+    f32x4 b[NBL];
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < NBL; ++j) {
+      const int64_t col = colW + piece_col(j, lane);
+      b[j] = col < p.N ? bias4(p, col, p.N - col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t col = n0 + colL + 32 * j + 8 * q;
-        b[j][q] = col < p.N ? bias4(p, col, p.N - col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-      }
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int j = 0; j < NBL; ++j) {
+        const int R = wm * WTM + piece_row(i, lane), Cc = wn * WTN + piece_col(j, lane);
+        MHG_LDS u32x2 *at = reinterpret_cast<MHG_LDS u32x2 *>(size_t(prior_at(R, Cc >> 3) + 8 * ((Cc >> 2) & 1)));
+        const u32x2 h = *at;
+        f32x4 c;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int R = wm * WTM + 32 * i + (lane & 31), Cc = colL + 32 * j + 8 * q;
-          MHG_LDS u32x2 *at = reinterpret_cast<MHG_LDS u32x2 *>(size_t(prior_at(R, Cc >> 3) + 8 * ((Cc >> 2) & 1)));
-          const u32x2 h = *at;
-          f32x4 c;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint16_t u = uint16_t(h[e >> 1] >> (16 * (e & 1)));
-            c[e] = p.out_code == E_F16 ? float(__builtin_bit_cast(_Float16, u)) : float(__builtin_bit_cast(__bf16, u));
-          }
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          const f32x4 f = epilogue4pb(p, v, c, b[j][q], 4);
-          uint16_t o[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            o[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)f[e]) : __builtin_bit_cast(uint16_t, (__bf16)f[e]);
-          *at = u32x2{uint32_t(o[0]) | (uint32_t(o[1]) << 16), uint32_t(o[2]) | (uint32_t(o[3]) << 16)};
-          MHG_ORDER();     // one piece at a time: hoisting every read would spill
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t u = uint16_t(h[e >> 1] >> (16 * (e & 1)));
+          c[e] = p.out_code == E_F16 ? float(__builtin_bit_cast(_Float16, u)) : float(__builtin_bit_cast(__bf16, u));
         }
+        const f32x4 f = epilogue4pb(p, acc[i][j], c, b[j], 4);
+        uint16_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          o[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)f[e]) : __builtin_bit_cast(uint16_t, (__bf16)f[e]);
+        *at = u32x2{uint32_t(o[0]) | (uint32_t(o[1]) << 16), uint32_t(o[2]) | (uint32_t(o[3]) << 16)};
+        MHG_ORDER();     // one piece at a time: hoisting every read would spill
+      }
 #pragma unroll
     for (int k = 0; k < WTM / 8; ++k) {
       const int rr = 8 * k + (lane >> 3), cc = lane & 7;

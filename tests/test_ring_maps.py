@@ -11,11 +11,11 @@ the previous phase (complete before the barrier in between).
 import pytest
 
 GROUP, LOADS = 4, 4
-BK, BN, FN, STEPS = 32, 256, 2, 2     # 256 x 256 tile: 32-deep slabs, 2 B blocks a wave
+BK, BN, NBL, WTN = 32, 256, 4, 64     # 256 x 256 tile: 32-deep slabs, 4 B blocks of 16 a wave
 
 
 def kswz(bk, r):
-    return (r >> 2) & 3 if bk == 32 else (r >> 1) & 7 if bk == 64 else r & 15
+    return 2 * ((r >> 3) & 1) if bk == 32 else (r >> 1) & 7 if bk == 64 else r & 15
 
 
 def kc_off(bk, r, c):
@@ -50,14 +50,14 @@ def loaded_rows(wave, own):
 
 
 def read_bytes(wn):
-    """LDS bytes of the B slab read by a wave whose block of C is column block wn."""
+    """LDS bytes of the B slab read by a wave whose block of C is column block wn (one
+    16-byte read per 16-column block and lane: row 16 j + l % 16, k chunk l / 16)."""
     out = set()
     for lane in range(64):
-        base = kc_off(BK, lane & 31, lane >> 5) + 64 * BK * FN * wn
-        for s in range(STEPS):
-            for j in range(FN):
-                a = (base ^ (32 * s)) + 64 * BK * j
-                out.update(range(a, a + 16))
+        base = kc_off(BK, lane & 15, lane >> 4) + 2 * BK * WTN * wn
+        for j in range(NBL):
+            a = base + 32 * BK * j
+            out.update(range(a, a + 16))
     return out
 
 
