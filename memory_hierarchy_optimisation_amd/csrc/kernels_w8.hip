@@ -2,9 +2,9 @@
 // SIMD) in a ping-pong schedule, both operands loaded straight into a five-slot LDS
 // ring of K slabs.  Three tile shapes:
 //   * 256 x 256, 32-deep slabs: the two wave groups split the tile's rows, each wave
-//     owns 128 x 64 of C (4 x 2 accumulators of 32 x 32);
+//     owns 128 x 64 of C (8 x 4 accumulators of 16 x 16);
 //   * 128 x 128, 64-deep slabs: the two wave groups take alternate slabs (group 0 the
-//     even ones, group 1 the odd ones), each wave owns 64 x 64 of C (2 x 2
+//     even ones, group 1 the odd ones), each wave owns 64 x 64 of C (4 x 4
 //     accumulators), and the two partial sums of a block are added through LDS at the
 //     end;
 //   * 64 x 64, 128-deep slabs: as 128 x 128, with 32 x 32 of C per wave.
@@ -33,10 +33,11 @@
 //     1.76 GHz; these kernels at 4096^3: 1.74-1.77 vs 1.51-1.63 GHz).
 // Ping-pong: the waves form two groups, one wave of each per SIMD.  Block barriers
 // cut time into phases; in each phase one group runs the matrix instructions of a
-// slab back to back, with no memory instruction among them, while the other group
-// reads its fragments of the next slab from LDS and issues loads (at 256 x 256 each
-// group loads one operand of every slab; at 128 x 128 both operands of its own slabs).
-// Either way a phase holds 16 matrix instructions per wave.  A
+// slab back to back while the other group reads its fragments of the next slab from
+// LDS (at 256 x 256 each group also loads one operand of every slab in its memory
+// phase; at 128 x 128 and 64 x 64 a group requests both operands of its own slabs
+// between its matrix instructions).  A phase holds 32 matrix instructions per wave (16
+// at 64 x 64).  A
 // wave that interleaves its own loads with its matrix instructions stalls at them, and
 // a SIMD whose two waves do the same thing at the same time stalls with them; here the
 // matrix pipe of every SIMD is fed by one wave while the other waits on memory.
@@ -448,7 +449,7 @@ struct W8Gemm {
     wait_lgkm<0>();
     MHG_ORDER();
   }
-  // Compute phase: the wave's STEPS FM FN matrix instructions of a slab, back to back.
+  // Compute phase: the wave's STEPS MB NBL matrix instructions of a slab, back to back.
   // Groups on alternate slabs (ALT) request both operands of their slab t + 4 here, one
   // request after every few matrix instructions: slab t + 4's slot held slab t - 1,
   // which the other group finished reading two phases ago, and the compute phase has
