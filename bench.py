@@ -24,6 +24,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -53,13 +54,25 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_CODE_TOKENS = re.compile(r'"(?:\\.|[^"\\])*"|\'(?:\\.|[^\'\\])*\'|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_only(text):
+    """C/C++ source with its comments removed and runs of whitespace collapsed (string
+    and character literals are kept as they are)."""
+    kept = _CODE_TOKENS.sub(lambda m: m.group(0) if m.group(0)[0] in "\"'" else " ", text)
+    return re.sub(r"\s+", " ", kept).strip()
+
+
 def kernel_source_digest():
-    """Digest of the kernel sources; profile figures carry it so stale ones are ignored."""
+    """Digest of the code of the kernel sources (comments and layout whitespace removed):
+    profile figures carry it, so figures taken on other code are ignored, while an edit
+    of a comment leaves them valid."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "memory_hierarchy_optimisation_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as fh:
-            h.update(name.encode() + b"\0" + fh.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as fh:
+            h.update(name.encode() + b"\0" + code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
