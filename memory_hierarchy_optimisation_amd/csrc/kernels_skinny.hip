@@ -184,14 +184,18 @@ struct Skinny {
     //
     // Visibility across the XCDs' separate L2 caches without a device-wide fence (an
     // agent-scope release writes back the whole L2 and cost more than the product
-    // itself once every workgroup issued one): the partials are written with the
-    // device-scope cache policy (sc1, as the compiler does for agent-scope atomic
-    // stores), which writes through to the coherent level; each lane waits for its
-    // stores to be acknowledged (vmcnt 0: the ordering part of a release, the L2
-    // write-back part being needed only for ordinary stores); the workgroup barrier
-    // then precedes the arrival RMW, and the last arrival reads the partials back with
-    // the same policy (served from the coherent level), issued only after its RMW
-    // returned.
+    // itself once every workgroup issued one).  The LLVM AMDGPU backend's memory model
+    // for gfx942/gfx950 encodes a relaxed agent-scope atomic store or load as the plain
+    // access with the sc1 bit, an agent-scope release as an L2 write-back (buffer_wbl2
+    // sc1) followed by a wait for all outstanding memory accesses (vmcnt 0), and an
+    // agent-scope acquire as that wait followed by an L2 invalidate (buffer_inv sc1);
+    // the write-back and the invalidate exist for ordinary accesses only.  So: the
+    // partials are written as agent-scope atomic stores (sc1 buffer stores, written
+    // through to the coherent level); each lane waits for them to be acknowledged
+    // (vmcnt 0, the release's ordering part; __syncthreads alone does not wait for
+    // them); the workgroup barrier then precedes the arrival RMW; and the last arrival
+    // reads the partials back as agent-scope atomic loads (sc1), issued only after its
+    // RMW returned.  No ordinary access touches the workspace.
     unsigned *count = static_cast<unsigned *>(p.workspace);
     const float *part = reinterpret_cast<const float *>(static_cast<char *>(p.workspace) +
                                                         ((int64_t(gn) * 4 + 255) / 256) * 256);
