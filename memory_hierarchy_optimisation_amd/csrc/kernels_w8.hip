@@ -638,27 +638,34 @@ struct W8Gemm {
     barrier();
     MHG_ORDER();
 
-    if (TL::KSPLIT == 2) {
-      // Group 1 hands its partial sums to its partner wave of group 0 (same block of C)
-      // through LDS, lane-major so that neither side has bank conflicts.
+    if constexpr (TL::KSPLIT == 2) {
+      // The two waves that hold partial sums of one block of C (wave gw of each group)
+      // finish half of its rows each: group 0 the 16-row blocks i < MB/2, group 1 the
+      // others.  Each hands the half its partner finishes through LDS, lane-major so that
+      // neither side has bank conflicts, and adds the half it receives (the sum of the
+      // two partials is the same either way round).  All eight waves then run the
+      // epilogue on half a block each, staging in 8 KiB past the hand-off areas.
+      constexpr int H2 = MB / 2;
       const uint32_t handoff = lds0 + gw * (MB * NBL * 64 * 16);
-      if (grp == 1) {
-#pragma unroll
-        for (int i = 0; i < MB; ++i)
-#pragma unroll
-          for (int j = 0; j < NBL; ++j)
-            *reinterpret_cast<MHG_LDS f32x4 *>(size_t(handoff + ((i * NBL + j) * 64 + lane) * 16)) = acc[i][j];
-      }
-      barrier();
-      if (grp == 1) return;
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NBL; ++j)
-          acc[i][j] += *reinterpret_cast<const MHG_LDS f32x4 *>(size_t(handoff + ((i * NBL + j) * 64 + lane) * 16));
+          if ((i < H2) == (grp == 1))
+            *reinterpret_cast<MHG_LDS f32x4 *>(size_t(handoff + ((i * NBL + j) * 64 + lane) * 16)) = acc[i][j];
+      barrier();
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NBL; ++j)
+          if ((i < H2) == (grp == 0))
+            acc[i][j] += *reinterpret_cast<const MHG_LDS f32x4 *>(size_t(handoff + ((i * NBL + j) * 64 + lane) * 16));
+      static_assert(4 * MB * NBL * 1024 <= 65536 && 65536 + 8 * 8192 <= SLOTS * SLOT_BYTES, "hand-off and staging");
+      if (grp == 0) epilogue<0, H2>(lane, lds0 + 65536 + wave * 8192);
+      else epilogue<H2, H2>(lane, lds0 + 65536 + wave * 8192);
+    } else {
+      epilogue<0, MB>(lane, lds0 + wave * 16384);
     }
-    // Staging areas: past the hand-off areas (4 x 16 KiB) when the groups split K.
-    epilogue(lane, TL::KSPLIT == 2 ? lds0 + 65536 + gw * 16384 : lds0 + wave * 16384);
   }
 
   // acc[i][j] holds the transposed 16 x 16 block (B's fragment is the instruction's
@@ -669,16 +676,20 @@ struct W8Gemm {
   // 64-column row segments of C.
   static __device__ __forceinline__ int piece_row(int i, int lane) { return 16 * i + (lane & 15); }
   static __device__ __forceinline__ int piece_col(int j, int lane) { return 16 * j + 4 * (lane >> 4); }
+  // The epilogue on the wave's 16-row blocks I0 .. I0 + NI - 1 (all of them, or half
+  // when the groups split K), staged at `region` (16 NI rows of 256 bytes at most).
+  template <int I0, int NI>
   __device__ __forceinline__ void epilogue(int lane, uint32_t region) {
-    const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
+    const int64_t rowW = m0 + wm * WTM + 16 * I0, colW = n0 + wn * WTN;
     const int ob = p.out_code == E_F32 ? 4 : 2;
     if constexpr (PRIOR) {
+      static_assert(I0 == 0 && NI == MB, "the prior-C epilogue takes the whole block");
       epilogue_prior(lane);
       return;
     }
-    // Staging is laid out for 64-column blocks of 64 or 128 rows; the 32 x 32 blocks of
-    // the 64 x 64 tile (2 KiB of C a wave) store directly.
-    constexpr bool STAGE = FN == 2 && FM % 2 == 0;
+    // Staging is laid out for 64-column row segments (32 or more rows); the 32 x 32
+    // blocks of the 64 x 64 tile (2 KiB of C a wave) store directly.
+    constexpr bool STAGE = FN == 2 && NI % 2 == 0;
     const bool c16 = ((uintptr_t(p.C) | uintptr_t(p.ldc * ob)) & 15) == 0;
     if (STAGE && c16) {
       // A fused epilogue that reads the prior C (beta != 0), or that writes fp32, runs in
@@ -695,26 +706,29 @@ struct W8Gemm {
           b[j] = col < p.N ? bias4(p, col, p.N - col) : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int i = I0; i < I0 + NI; ++i)
 #pragma unroll
           for (int j = 0; j < NBL; ++j) acc[i][j] = epilogue4pb(p, acc[i][j], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, b[j], 4);
       }
       if (p.out_code == E_F32 || (p.epi && p.beta != 0.0f)) {
-        // 64 rows of 256 bytes a pass; chunk c of row r at 16 (c ^ (r % 16)), which keeps
-        // the 16-byte writes (16 rows at 4 chunks) and the read-back (4 rows at 16
-        // chunks) free of bank conflicts
+        // Up to 64 rows (nb blocks) of 256 bytes a pass; chunk c of row r at
+        // 16 (c ^ (r % 16)), which keeps the 16-byte writes (16 rows at 4 chunks) and the
+        // read-back (4 rows at 16 chunks) free of bank conflicts
 #pragma unroll
-        for (int pass = 0; pass < FM / 2; ++pass) {
+        for (int pass = 0; pass < (NI + 3) / 4; ++pass) {
+          const int nb = NI - 4 * pass < 4 ? NI - 4 * pass : 4;
 #pragma unroll
           for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
             for (int j = 0; j < NBL; ++j) {
+              if (i4 >= nb) break;
               const int r = piece_row(i4, lane), c = piece_col(j, lane) >> 2;
-              *reinterpret_cast<MHG_LDS f32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15)))) = acc[4 * pass + i4][j];
+              *reinterpret_cast<MHG_LDS f32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15)))) = acc[I0 + 4 * pass + i4][j];
             }
           if (!p.epi) {
 #pragma unroll
             for (int k = 0; k < 16; ++k) {
+              if (k >= 4 * nb) break;
               const int r = 4 * k + (lane >> 4), c = lane & 15;
               const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 256 + 16 * (c ^ (r & 15))));
               store_chunk(rowW + 64 * pass + r, colW + 4 * c, v, 4, rowW, colW);
@@ -727,12 +741,14 @@ struct W8Gemm {
           f32x4 prior[16];
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
+            if (k >= 4 * nb) break;
             const int64_t row = rowW + 64 * pass + 4 * k + (lane >> 4);
             prior[k] = p.beta != 0.0f && row < p.M && colB < p.N ? prior4(p, row, colB, p.N - colB)
                                                                  : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           }
 #pragma unroll
           for (int k = 0; k < 16; ++k) {
+            if (k >= 4 * nb) break;
             const int r = 4 * k + (lane >> 4), c = lane & 15;
             const int64_t row = rowW + 64 * pass + r, n_in = p.N - colB;
             if (row >= p.M || n_in <= 0) continue;
@@ -745,20 +761,20 @@ struct W8Gemm {
         // 128 bytes a row; chunk c of row r at 16 (c ^ ((r / 2) % 8)); a lane's piece is
         // half a chunk
 #pragma unroll
-        for (int i = 0; i < MB; ++i)
+        for (int i = 0; i < NI; ++i)
 #pragma unroll
           for (int j = 0; j < NBL; ++j) {
             const int r = piece_row(i, lane), col = piece_col(j, lane);
             uint16_t h[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              h[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)acc[i][j][e])
-                                         : __builtin_bit_cast(uint16_t, (__bf16)acc[i][j][e]);
+              h[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)acc[I0 + i][j][e])
+                                         : __builtin_bit_cast(uint16_t, (__bf16)acc[I0 + i][j][e]);
             const u32x2 v = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
             *reinterpret_cast<MHG_LDS u32x2 *>(size_t(region + r * 128 + 16 * ((col >> 3) ^ ((r >> 1) & 7)) + 2 * (col & 7))) = v;
           }
 #pragma unroll
-        for (int k = 0; k < WTM / 8; ++k) {
+        for (int k = 0; k < 2 * NI; ++k) {
           const int r = 8 * k + (lane >> 3), c = lane & 7;
           const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 128 + 16 * (c ^ ((r >> 1) & 7))));
           store_chunk(rowW + r, colW + 8 * c, v, 8, rowW, colW);
@@ -768,7 +784,7 @@ struct W8Gemm {
     }
     const bool c_vec = p.c_vec != 0;
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
+    for (int i = 0; i < NI; ++i) {
       const int64_t row = rowW + piece_row(i, lane);
       if (row >= p.M) continue;
       // With an epilogue, the row block's bias and prior values are requested before its
@@ -778,7 +794,7 @@ struct W8Gemm {
 #pragma unroll
         for (int j = 0; j < NBL; ++j) {
           const int64_t col = colW + piece_col(j, lane);
-          ep[j] = col < p.N ? epilogue4(p, acc[i][j], row, col, p.N - col) : acc[i][j];
+          ep[j] = col < p.N ? epilogue4(p, acc[I0 + i][j], row, col, p.N - col) : acc[I0 + i][j];
         }
       }
 #pragma unroll
@@ -786,7 +802,7 @@ struct W8Gemm {
         const int64_t col = colW + piece_col(j, lane);
         const int64_t n_in = p.N - col;
         if (n_in <= 0) continue;
-        store_out4(p.C, row * p.ldc + col, p.epi ? ep[j] : acc[i][j], p.out_code, c_vec && n_in >= 4, int(n_in));
+        store_out4(p.C, row * p.ldc + col, p.epi ? ep[j] : acc[I0 + i][j], p.out_code, c_vec && n_in >= 4, int(n_in));
       }
     }
   }
