@@ -432,6 +432,23 @@ struct W8Gemm {
     wait_lgkm<0>();
     MHG_ORDER();
   }
+  // One of the last four iterations of the 256 x 256 loop without the prior C: the
+  // memory phase requests nothing, and each wave waits until at most W of its loads are
+  // in flight (those of the slabs after slab t + 1).
+  template <int W>
+  __device__ __forceinline__ void last_iter(int t) {
+    fa_cur = fa_off[0];
+    mem_steps<0>(slot_addr(t), slot_addr(t));
+    wait_lgkm<0>();
+    MHG_ORDER();
+    wait_vm<W>();
+    barrier();
+    MHG_ORDER();
+    compute();
+    wait_vm<W>();
+    barrier();
+    MHG_ORDER();
+  }
   template <bool PAST = false>
   __device__ __forceinline__ void mem(int t) {
     fa_cur = fa_off[0];
@@ -585,8 +602,11 @@ struct W8Gemm {
       barrier();
       if (grp == 1) barrier();
       MHG_ORDER();
-      // The last four iterations request the slabs past K; a loop of their own keeps
-      // the choice of what those load (zeros, or the prior C) out of the main loop.
+      // The last four iterations would request the slabs past K.  With the prior C they
+      // load it; otherwise they request nothing, and each waits for exactly the slabs
+      // still in flight that the next phase needs (a wave's loads complete in the order
+      // issued).  Fewer than four slabs keep the uniform form, the prologue having
+      // requested zeros past K.
       int t = 0;
       for (; t < KT - AHEAD; ++t) {
         mem(t);
@@ -597,6 +617,14 @@ struct W8Gemm {
         wait_vm<3 * LOADS>();
         barrier();
         MHG_ORDER();
+      }
+      if (!PRIOR && KT >= AHEAD) {
+        static_assert(AHEAD == 4, "tail of four iterations");
+        last_iter<2 * LOADS>(t);
+        last_iter<LOADS>(t + 1);
+        last_iter<0>(t + 2);
+        last_iter<0>(t + 3);
+        t = KT;
       }
       for (; t < KT; ++t) {
         mem<true>(t);
