@@ -786,26 +786,47 @@ struct W8Gemm {
           }
         }
       } else {
-        // 128 bytes a row; chunk c of row r at 16 (c ^ ((r / 2) % 8)); a lane's piece is
-        // half a chunk
+        // A lane's converted piece (four columns, 8 bytes) of block 2 i2 and the one of
+        // block 2 i2 + 1 (rows t and 16 + t of the pair, same columns) go out as one
+        // 16-byte write.  8-byte writes are served 16 consecutive lanes at a time within
+        // 128 bytes of banks, where 16 rows at one column offset can reach only 8 places;
+        // 16-byte writes are served 16 lanes at a time over all 256 bytes.  The unit of
+        // lane (t, g) for (i2, j) sits at slot 16 g + (t ^ (4 j + 2 (g / 2) + g % 2)) of that
+        // pair and column block's 1 KiB.  The read-back takes a 16-byte row chunk as its
+        // two 8-byte pieces (8-byte reads: 32 consecutive lanes a pass), each store
+        // instruction covering four rows of each half of a pair, so that a pass reads
+        // both halves of its units: no bank conflicts on either side.  (Column groups
+        // g and g + 1 differ in the low bit of the slot as well, so that the two reads
+        // are not a constant distance apart: the compiler fused such a pair into one
+        // two-address read, and the conflict counter showed that form conflicting here,
+        // 8 cycles an instruction; the two separate reads show none.)
+        static_assert(!STAGE || (NI % 2 == 0 && NBL == 4), "pairs of 16-row blocks, 64 columns");
+        const int t = lane & 15, g = lane >> 4;
+        const auto half = [&](f32x4 a) {
+          uint16_t h[4];
 #pragma unroll
-        for (int i = 0; i < NI; ++i)
+          for (int e = 0; e < 4; ++e)
+            h[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)a[e])
+                                       : __builtin_bit_cast(uint16_t, (__bf16)a[e]);
+          return u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+        };
+#pragma unroll
+        for (int i2 = 0; i2 < NI / 2; ++i2)
 #pragma unroll
           for (int j = 0; j < NBL; ++j) {
-            const int r = piece_row(i, lane), col = piece_col(j, lane);
-            uint16_t h[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              h[e] = p.out_code == E_F16 ? __builtin_bit_cast(uint16_t, (_Float16)acc[I0 + i][j][e])
-                                         : __builtin_bit_cast(uint16_t, (__bf16)acc[I0 + i][j][e]);
-            const u32x2 v = {uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
-            *reinterpret_cast<MHG_LDS u32x2 *>(size_t(region + r * 128 + 16 * ((col >> 3) ^ ((r >> 1) & 7)) + 2 * (col & 7))) = v;
+            const u32x2 lo = half(acc[I0 + 2 * i2][j]), hi = half(acc[I0 + 2 * i2 + 1][j]);
+            const uint32_t slot = uint32_t((i2 * NBL + j) * 64 + 16 * g + (t ^ (4 * j + 2 * (g >> 1) + (g & 1))));
+            *reinterpret_cast<MHG_LDS u32x4 *>(size_t(region + 16 * slot)) = u32x4{lo.x, lo.y, hi.x, hi.y};
           }
 #pragma unroll
         for (int k = 0; k < 2 * NI; ++k) {
-          const int r = 8 * k + (lane >> 3), c = lane & 7;
-          const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(region + r * 128 + 16 * (c ^ ((r >> 1) & 7))));
-          store_chunk(rowW + r, colW + 8 * c, v, 8, rowW, colW);
+          const int i2 = k >> 2, rho = lane >> 3, sh = rho & 1, tt = 4 * (k & 3) + (rho >> 1), c = lane & 7;
+          const int j = c >> 1, g0 = 2 * (c & 1);
+          const uint32_t u = uint32_t((i2 * NBL + j) * 64 + 16 * g0), f = uint32_t(4 * j + 2 * (c & 1));
+          const uint32_t at = region + 16 * (u + (tt ^ f)) + 8 * sh, at2 = region + 16 * (u + 16 + (tt ^ (f + 1))) + 8 * sh;
+          const u32x2 a = *reinterpret_cast<const MHG_LDS u32x2 *>(size_t(at));
+          const u32x2 b = *reinterpret_cast<const MHG_LDS u32x2 *>(size_t(at2));
+          store_chunk(rowW + 32 * i2 + 16 * sh + tt, colW + 8 * c, u32x4{a.x, a.y, b.x, b.y}, 8, rowW, colW);
         }
       }
       return;

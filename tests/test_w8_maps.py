@@ -13,7 +13,10 @@ epilogue's staging) and check that:
   counter (one lane pair per dispatch at the same banks, the other lanes
   broadcasting): a 16-byte read goes in four passes, each the four-lane quads of one
   half-wave whose quad index has the same parity (lanes 0-3, 12-15, 20-23, 24-27 for
-  lane 0); an 8-byte transpose read in two passes of 32 consecutive lanes;
+  lane 0); an 8-byte read (plain or transpose) in two passes of 32 consecutive lanes;
+  an 8-byte write in four passes of 16 consecutive lanes, whose banks repeat every 128
+  bytes (measured with only the two lanes of the pair active, the method checked
+  against the known 16-byte grouping);
 * the epilogue's staging writes every element of a wave's block of C once, and the
   store loop reads it back at the right row and column.
 """
@@ -228,73 +231,141 @@ def piece(i, j, lane):
     return 16 * i + (lane & 15), 16 * j + 4 * (lane >> 4)
 
 
+# The blocks a wave finishes: all of them, or (128 x 128, where the two groups split K)
+# half each, the first or the second.
+def _parts(tile):
+    _, _, _, FM, FN = TILES[tile]
+    MB = 2 * FM
+    return [(0, MB)] + ([(0, MB // 2), (MB // 2, MB // 2)] if tile == 128 else [])
+
+
 @pytest.mark.parametrize("tile", [256, 128])
 def test_fp32_staging_round_trip(tile):
     _, _, _, FM, FN = TILES[tile]
-    MB, NBL = 2 * FM, 2 * FN
-    for pas in range(FM // 2):
-        region = {}
-        for lane in range(64):
-            for i4 in range(4):
-                for j in range(NBL):
-                    r, col = piece(i4, j, lane)
-                    c = col >> 2
-                    addr = r * 256 + 16 * (c ^ swz16(r))
-                    assert addr not in region
-                    row, col0 = piece(4 * pas + i4, j, lane)
-                    region[addr] = [(row, col0 + e) for e in range(4)]
-        assert len(region) == 64 * 16
-        for lane in range(64):
-            for k in range(16):
-                r, c = 4 * k + (lane >> 4), lane & 15
-                got = region[r * 256 + 16 * (c ^ swz16(r))]
-                assert got == [(64 * pas + r, 4 * c + e) for e in range(4)]
+    NBL = 2 * FN
+    for I0, NI in _parts(tile):
+        for pas in range((NI + 3) // 4):
+            nb = min(4, NI - 4 * pas)
+            region = {}
+            for lane in range(64):
+                for i4 in range(nb):
+                    for j in range(NBL):
+                        r, col = piece(i4, j, lane)
+                        c = col >> 2
+                        addr = r * 256 + 16 * (c ^ swz16(r))
+                        assert addr not in region
+                        row, col0 = piece(I0 + 4 * pas + i4, j, lane)
+                        region[addr] = [(row, col0 + e) for e in range(4)]
+            assert len(region) == 64 * 4 * nb
+            for lane in range(64):
+                for k in range(4 * nb):
+                    r, c = 4 * k + (lane >> 4), lane & 15
+                    got = region[r * 256 + 16 * (c ^ swz16(r))]
+                    assert got == [(16 * I0 + 64 * pas + r, 4 * c + e) for e in range(4)]
+
+
+def stage16_slot(i2, j, lane):
+    """16-byte unit of a lane's pieces of blocks 2 i2 and 2 i2 + 1 in column block j."""
+    t, g = lane & 15, lane >> 4
+    return (i2 * 4 + j) * 64 + 16 * g + (t ^ (4 * j + 2 * (g >> 1) + (g & 1)))
+
+
+def stage16_read(k, lane):
+    """Store instruction k of the 16-bit read-back: (row, first column, the two 8-byte
+    piece addresses) of a lane."""
+    i2, rho, c = k >> 2, lane >> 3, lane & 7
+    sh, tt = rho & 1, 4 * (k & 3) + (rho >> 1)
+    j = c >> 1
+    u, f = (i2 * 4 + j) * 64 + 16 * (2 * (c & 1)), 4 * j + 2 * (c & 1)
+    return 32 * i2 + 16 * sh + tt, 8 * c, (16 * (u + (tt ^ f)) + 8 * sh, 16 * (u + 16 + (tt ^ (f + 1))) + 8 * sh)
 
 
 @pytest.mark.parametrize("tile", [256, 128])
 def test_16bit_staging_round_trip(tile):
-    _, _, _, FM, FN = TILES[tile]
-    MB, NBL, WTM = 2 * FM, 2 * FN, 32 * FM
-    region = {}
-    for lane in range(64):
-        for i in range(MB):
-            for j in range(NBL):
-                r, col = piece(i, j, lane)
-                addr = r * 128 + 16 * ((col >> 3) ^ swz8(r)) + 2 * (col & 7)
-                for e in range(4):
-                    assert addr + 2 * e not in region
-                    region[addr + 2 * e] = (r, col + e)
-    assert len(region) == WTM * 64
-    for lane in range(64):
-        for k in range(WTM // 8):
-            r, c = 8 * k + (lane >> 3), lane & 7
-            base = r * 128 + 16 * (c ^ swz8(r))
-            assert [region[base + 2 * e] for e in range(8)] == [(r, 8 * c + e) for e in range(8)]
+    for I0, NI in _parts(tile):
+        region = {}
+        for lane in range(64):
+            for i2 in range(NI // 2):
+                for j in range(4):
+                    base = 16 * stage16_slot(i2, j, lane)
+                    for s in range(2):
+                        r, col = piece(2 * i2 + s, j, lane)
+                        for e in range(4):
+                            a = base + 8 * s + 2 * e
+                            assert a not in region
+                            region[a] = (r, col + e)
+        assert len(region) == 16 * NI * 64
+        rows = set()
+        for k in range(2 * NI):
+            for lane in range(64):
+                row, col, (a0, a1) = stage16_read(k, lane)
+                got = [region[a0 + 2 * e] for e in range(4)] + [region[a1 + 2 * e] for e in range(4)]
+                assert got == [(row, col + e) for e in range(8)]
+                rows.add(row)
+        assert rows == set(range(16 * NI))
+        # every store instruction writes whole 128-byte rows: 8 rows of 8 chunks
+        for k in range(2 * NI):
+            got = sorted((stage16_read(k, l)[0], stage16_read(k, l)[1]) for l in range(64))
+            assert len({r for r, _ in got}) == 8 and all(c in range(0, 64, 8) for _, c in got)
+
+
+def _banks128(addr, nbytes):
+    return {((addr + o) // 4) % 32 for o in range(0, nbytes, 4)}
+
+
+def _write8_conflict_free(addresses):
+    """An 8-byte write pass: 16 consecutive lanes within 128 bytes of banks."""
+    seen = set()
+    for a in addresses:
+        b = _banks128(a, 8)
+        if seen & b:
+            return False
+        seen |= b
+    return True
 
 
 @pytest.mark.parametrize("tile", [256, 128])
 def test_staging_writes_are_conflict_free(tile):
     _, _, _, FM, FN = TILES[tile]
     MB, NBL = 2 * FM, 2 * FN
-    for i in range(MB if FM else 0):
+    for i in range(MB):
         for j in range(NBL):
-            a32, a16 = [], []
+            a32 = []
             for lane in range(64):
                 r, col = piece(i % 4, j, lane)
                 a32.append(r * 256 + 16 * ((col >> 2) ^ swz16(r)))
-                r, col = piece(i, j, lane)
-                a16.append(r * 128 + 16 * ((col >> 3) ^ swz8(r)) + 2 * (col & 7))
             for grp in _passes16(a32):
                 assert _conflict_free(grp, 16)
-            for h in range(2):
-                assert _conflict_free(a16[32 * h:32 * h + 32], 8)
-    # the read-backs: 4 rows at 16 chunks (fp32), 8 rows at 8 chunks (16-bit)
+    for i2 in range(MB // 2):
+        for j in range(NBL):
+            a16 = [16 * stage16_slot(i2, j, l) for l in range(64)]
+            for grp in _passes16(a16):
+                assert _conflict_free(grp, 16), (i2, j)
+    # the read-backs: 4 rows at 16 chunks (fp32); 8-byte piece pairs (16-bit)
     for k in range(16):
         rb = [(4 * k + (l >> 4)) * 256 + 16 * ((l & 15) ^ swz16(4 * k + (l >> 4))) for l in range(64)]
         assert all(_conflict_free(g, 16) for g in _passes16(rb))
-    for k in range(16):
-        rb = [(8 * k + (l >> 3)) * 128 + 16 * ((l & 7) ^ swz8(8 * k + (l >> 3))) for l in range(64)]
-        assert all(_conflict_free(g, 16) for g in _passes16(rb))
+    for k in range(MB * 2):
+        for e in range(2):
+            rb = [stage16_read(k, l)[2][e] for l in range(64)]
+            for half in range(2):
+                assert _conflict_free(rb[32 * half:32 * half + 32], 8), (k, e, half)
+
+
+def test_8byte_staging_writes_would_conflict():
+    # The earlier 16-bit staging: 128-byte rows, chunk c of row r at 16 (c ^ ((r / 2) % 8)),
+    # each lane writing its 8-byte piece of one block.  Conflict-free in 32-lane passes
+    # over 256 bytes, but the measured 8-byte write passes (16 lanes, 128 bytes of
+    # banks) put rows t and t ^ 1 on the same banks: one extra cycle a pass, the
+    # 262 144 conflict cycles the counter showed at 4096^3 (four per write instruction).
+    for i in range(8):
+        for j in range(4):
+            addrs = []
+            for lane in range(64):
+                r, col = piece(i, j, lane)
+                addrs.append(r * 128 + 16 * ((col >> 3) ^ swz8(r)) + 2 * (col & 7))
+            assert all(_conflict_free(addrs[32 * h:32 * h + 32], 8) for h in range(2))
+            assert not any(_write8_conflict_free(addrs[16 * q:16 * q + 16]) for q in range(4))
 
 
 def test_direct_store_pieces_cover_the_block():
