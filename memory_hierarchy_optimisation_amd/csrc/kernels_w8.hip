@@ -472,6 +472,7 @@ struct W8Gemm {
   // which the other group finished reading two phases ago, and the compute phase has
   // room for the requests that the memory phase has not (2048^3 NT 26.1 -> 25.6 us,
   // 1024^3 9.3-9.7 -> 8.8-8.9 us, 1000^3 10.1-10.3 -> 9.7 us on one box).
+  template <bool ISSUE = true>
   __device__ __forceinline__ void compute(int t = 0) {
     constexpr int NMF = STEPS * MB * NBL, EVERY = NMF / (2 * LOADS);
     static_assert(!ALT || (EVERY >= 1 && NMF % (2 * LOADS) == 0), "requests spread over the matrix instructions");
@@ -481,7 +482,7 @@ struct W8Gemm {
     for (int s = 0; s < STEPS; ++s)
 #pragma unroll
       for (int m = 0; m < MB * NBL; ++m) {
-        if constexpr (ALT) {
+        if constexpr (ALT && ISSUE) {
           const int n = s * MB * NBL + m;
           if (n % EVERY == EVERY - 1) {
             const int q = n / EVERY;
@@ -648,7 +649,11 @@ struct W8Gemm {
       barrier();
       if (grp == 1) barrier();
       MHG_ORDER();
-      for (int u = 0; u < (KT + 1) / 2; ++u) {
+      // The slabs the group's last two iterations would request are never multiplied:
+      // those iterations request nothing and wait for every load still in flight.
+      const int U = (KT + 1) / 2;
+      int u = 0;
+      for (; u < U - 2; ++u) {
         mem(2 * u + int(grp));
         wait_vm<4 * LOADS>();
         barrier();
@@ -658,10 +663,20 @@ struct W8Gemm {
         barrier();
         MHG_ORDER();
       }
+      for (; u < U; ++u) {
+        mem(2 * u + int(grp));
+        wait_vm<4 * LOADS>();
+        barrier();
+        MHG_ORDER();
+        compute<false>(2 * u + int(grp));
+        wait_vm<0>();
+        barrier();
+        MHG_ORDER();
+      }
     }
     if (grp == 0) barrier();
-    // Loads past K (zeros) are still writing LDS: drain them, then let every wave
-    // finish with the ring before the epilogue reuses its memory.
+    // Loads past K (zeros, or the prior C) may still be writing LDS: drain them, then let
+    // every wave finish with the ring before the epilogue reuses its memory.
     wait_vm<0>();
     barrier();
     MHG_ORDER();
