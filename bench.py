@@ -112,11 +112,14 @@ def clock_during(run, first):
     return 100.0 * cycles / ticks
 
 
-def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock=False, rotate=True):
+def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock=False, rotate=True,
+            settle_s=0.0):
     """Time `steps` calls after `settle` + `warmup` untimed calls.  Returns a dict of
-    figures.  epilogue: run through the fused epilogue with alpha = beta = 1, a bias and
-    ReLU (C is read as well as written; its bytes and the bias's count in the GB/s).
-    clock: afterwards, read the shader clock during a further run of calls."""
+    figures.  settle_s: before those, untimed calls in chunks of 50 until that many
+    seconds have passed (the clock's settling takes time, not a number of calls).
+    epilogue: run through the fused epilogue with alpha = beta = 1, a bias and ReLU (C is
+    read as well as written; its bytes and the bias's count in the GB/s).  clock:
+    afterwards, read the shader clock during a further run of calls."""
     import torch
 
     import memory_hierarchy_optimisation_amd as mh
@@ -150,7 +153,15 @@ def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock
         else:
             mh.gemm_run(plan, a_ptr[i % copies], b_ptr[i % copies], c_ptr, handle)
 
+    settled = 0
     try:
+        if settle_s > 0:
+            t_end = time.perf_counter() + settle_s
+            while time.perf_counter() < t_end:
+                for i in range(50):
+                    run(settled + i)
+                settled += 50
+                torch.cuda.synchronize()
         for i in range(settle + warmup):
             run(i)
         torch.cuda.synchronize()
@@ -190,7 +201,7 @@ def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock
         "layout": ("A col" if w.a_col else "A row") + (", B col" if w.b_col else ", B row"),
         "tile": f"{desc['bm']}x{desc['bn']}x{desc['bk']}", "kind": desc["kind"],
         "grid": desc["grid_x"] * desc["grid_y"] * desc["grid_z"], "rotated_copies": copies,
-        "settle_calls": settle, "warmup_calls": warmup, "timed_calls": steps,
+        "settle_calls": settle + settled, "warmup_calls": warmup, "timed_calls": steps,
         "ms_per_step": ms_step, "kernel_ms_event": event_ms,
         "tflops": flops / (ms_step / 1000.0) / 1e12,
         "kernel_tflops": flops / (event_ms / 1000.0) / 1e12,
@@ -603,9 +614,11 @@ def main():
     shapes = []
     if not args.no_per_shape:
         for name in PER_SHAPE:
-            # Small shapes too get a few hundred untimed calls first: the clock that the
-            # previous line left is not the one a steady stream of these calls settles to.
-            r = head if name == args.workload else measure(name, 300, 300, per_call=True)
+            # Every line settles first, for as long as the headline's settling calls take:
+            # the clock that the previous line left is not the one a steady stream of
+            # these calls settles to (with 300 untimed calls alone, ~7 ms at 2048^3, the
+            # timed batch still ran slower than the per-call groups after it).
+            r = head if name == args.workload else measure(name, 300, 300, per_call=True, settle_s=0.2)
             shapes.append(r)
             log(f"[bench] {name}: {r['kernel_tflops']:.1f} TFLOP/s, {r['kernel_gbps']:.0f} GB/s, "
                 f"{100 * r['frac_of_roofline']:.1f}% of the {r['bound']} roofline, tile {r['tile']}")
@@ -613,13 +626,13 @@ def main():
     if not args.no_per_shape and not args.no_extras:
         # The same settling as the headline and the per-shape lines' fixed warm-up: the
         # clock settles again after the smaller per-shape lines.
-        r = measure(args.workload, 100, 300, settle=SETTLE_CALLS, per_call=True, epilogue=True, clock=True)
+        r = measure(args.workload, 300, 300, settle=SETTLE_CALLS, per_call=True, epilogue=True, clock=True)
         extras["epilogue"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         log(f"[bench] {r['workload']} (alpha, beta = 1, bias, ReLU): {r['kernel_tflops']:.1f} TFLOP/s, "
             f"kernel {r['kernel_ms_event'] * 1000:.1f} us against {head['kernel_ms_event'] * 1000:.1f} us plain")
         # Context only: the same calls on one operand copy, which stays in the Infinity
         # Cache (the graded figure above streams its operands from HBM).
-        r = measure(args.workload, 100, 300, settle=SETTLE_CALLS, per_call=True, rotate=False)
+        r = measure(args.workload, 300, 300, settle=SETTLE_CALLS, per_call=True, rotate=False)
         extras["warm"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         log(f"[bench] {r['workload']}: {r['kernel_tflops']:.1f} TFLOP/s, kernel {r['kernel_ms_event'] * 1000:.1f} us")
         extras["autotune"] = autotune_report([n for n in PER_SHAPE if n != "f32_64"])
