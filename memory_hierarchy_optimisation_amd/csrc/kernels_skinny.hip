@@ -145,21 +145,24 @@ struct Skinny {
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));
 
     // acc[c] lane l: rows 4 g .. 4 g + 3 of column 8 q + c.  Waves' partials meet in
-    // LDS and are added in wave order.
+    // LDS and are added in wave order.  A row of red holds columns 8 u .. 8 u + 3 at
+    // float 4 u and 8 u + 4 .. 8 u + 7 at float 64 + 4 u, so that the 16 lanes an LDS
+    // pass serves touch 16 different 16-byte chunks of the 256 bytes of banks (at float
+    // 8 u, lanes u and u + 8 shared banks: half the LDS cycles were conflict cycles).
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      float *dst = &red[wave][4 * g + r][8 * q];
-      *reinterpret_cast<f32x4 *>(dst) = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
-      *reinterpret_cast<f32x4 *>(dst + 4) = f32x4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
+      float *dst = &red[wave][4 * g + r][0];
+      *reinterpret_cast<f32x4 *>(dst + 4 * q) = f32x4{acc[0][r], acc[1][r], acc[2][r], acc[3][r]};
+      *reinterpret_cast<f32x4 *>(dst + 64 + 4 * q) = f32x4{acc[4][r], acc[5][r], acc[6][r], acc[7][r]};
     }
     __syncthreads();
-    const int row = threadIdx.x >> 4, col = 8 * (threadIdx.x & 15);
-    f32x4 s0 = *reinterpret_cast<const f32x4 *>(&red[0][row][col]);
-    f32x4 s1 = *reinterpret_cast<const f32x4 *>(&red[0][row][col + 4]);
+    const int row = threadIdx.x >> 4, u = threadIdx.x & 15, col = 8 * u;
+    f32x4 s0 = *reinterpret_cast<const f32x4 *>(&red[0][row][4 * u]);
+    f32x4 s1 = *reinterpret_cast<const f32x4 *>(&red[0][row][64 + 4 * u]);
 #pragma unroll
     for (int w = 1; w < 4; ++w) {
-      s0 += *reinterpret_cast<const f32x4 *>(&red[w][row][col]);
-      s1 += *reinterpret_cast<const f32x4 *>(&red[w][row][col + 4]);
+      s0 += *reinterpret_cast<const f32x4 *>(&red[w][row][4 * u]);
+      s1 += *reinterpret_cast<const f32x4 *>(&red[w][row][64 + 4 * u]);
     }
     const int64_t cg = n0 + col;
     const bool c_vec = p.c_vec != 0;
