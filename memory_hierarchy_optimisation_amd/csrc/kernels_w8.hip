@@ -63,6 +63,8 @@
 // one rounding.  The 256 x 256 tile has a second instantiation for a 16-bit prior C:
 // the four slab requests past K load the prior C tile into the ring instead of zeros,
 // so its reads overlap the last slabs' arithmetic.
+#include <type_traits>
+
 #include "device.h"
 
 namespace mhg {
@@ -816,6 +818,11 @@ struct W8Gemm {
         // two-address read, and the conflict counter showed that form conflicting here,
         // 8 cycles an instruction; the two separate reads show none.)
         static_assert(!STAGE || (NI % 2 == 0 && NBL == 4), "pairs of 16-row blocks, 64 columns");
+        if (!p.epi && p.out_code == kHalfOut && rowW + 16 * NI <= p.M && colW + WTN <= p.N &&
+            (int64_t(16 * NI) * p.ldc + WTN) * 2 < (int64_t(1) << 31)) {
+          staged16_inside<I0, NI>(lane, region, rowW, colW);
+          return;
+        }
         const int t = lane & 15, g = lane >> 4;
         const auto half = [&](f32x4 a) {
           uint16_t h[4];
@@ -868,6 +875,59 @@ struct W8Gemm {
         if (n_in <= 0) continue;
         store_out4(p.C, row * p.ldc + col, p.epi ? ep[j] : acc[I0 + i][j], p.out_code, c_vec && n_in >= 4, int(n_in));
       }
+    }
+  }
+
+  // The 16-bit staged epilogue above for a wave block wholly inside C, with no fused
+  // epilogue: the same LDS layout and store pattern, with the arithmetic taken out of the
+  // per-write and per-store work (the epilogue runs on all waves of all compute units at
+  // once, two waves a SIMD, so every vector instruction counts: the general form took
+  // ~6 us a workgroup at 4096^3, most of it instruction issue).  The conversion is the
+  // output type's alone (16-bit output has the input's type); the four per-lane LDS
+  // write offsets and the read-back offsets are computed once, the rest being immediate
+  // offsets; the stores go through one buffer resource at the block's corner with a
+  // fixed per-lane offset, the row step (uniform) in the scalar offset.
+  static constexpr int kHalfOut = std::is_same<H, HalfBF16>::value ? E_BF16 : E_F16;
+  static __device__ __forceinline__ u32x2 pack_half(f32x4 a) {
+    uint16_t h[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      h[e] = std::is_same<H, HalfBF16>::value ? __builtin_bit_cast(uint16_t, (__bf16)a[e])
+                                              : __builtin_bit_cast(uint16_t, (_Float16)a[e]);
+    return u32x2{uint32_t(h[0]) | (uint32_t(h[1]) << 16), uint32_t(h[2]) | (uint32_t(h[3]) << 16)};
+  }
+  template <int I0, int NI>
+  __device__ __forceinline__ void staged16_inside(int lane, uint32_t region, int64_t rowW, int64_t colW) {
+    const int t = lane & 15, g = lane >> 4;
+    uint32_t woff[NBL];
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) woff[j] = region + 16 * uint32_t(64 * j + 16 * g + (t ^ (4 * j + 2 * (g >> 1) + (g & 1))));
+#pragma unroll
+    for (int i2 = 0; i2 < NI / 2; ++i2)
+#pragma unroll
+      for (int j = 0; j < NBL; ++j) {
+        const u32x2 lo = pack_half(acc[I0 + 2 * i2][j]), hi = pack_half(acc[I0 + 2 * i2 + 1][j]);
+        *reinterpret_cast<MHG_LDS u32x4 *>(size_t(woff[j] + uint32_t(16 * 64 * NBL * i2))) = u32x4{lo.x, lo.y, hi.x, hi.y};
+      }
+    // Store k: rows 32 (k / 4) + 16 sh + 4 (k % 4) + r2 of the block, columns 8 c ..;
+    // its two pieces at slot (k / 4) NBL 64 + 64 j + 16 (2 cb) + (tt ^ f) and 16 slots
+    // on with f + 1, tt = 4 (k % 4) + r2, f = 4 j + 2 cb, where tt ^ f = 4 ((k % 4) ^ j)
+    // + (r2 ^ 2 cb).
+    const int rho = lane >> 3, sh = rho & 1, r2 = rho >> 1, c = lane & 7, j = c >> 1, cb = c & 1;
+    const uint32_t rb = region + 16 * uint32_t(64 * j + 32 * cb + (r2 ^ (2 * cb))) + 8 * sh;
+    const uint32_t rb2 = region + 16 * uint32_t(64 * j + 32 * cb + 16 + (r2 ^ (2 * cb + 1))) + 8 * sh;
+    uint32_t qo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) qo[q] = 64 * uint32_t(q ^ j);
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(static_cast<const char *>(p.C) + (rowW * p.ldc + colW) * 2);
+    const uint32_t voff = uint32_t(((16 * sh + r2) * p.ldc + 8 * c) * 2);
+#pragma unroll
+    for (int k = 0; k < 2 * NI; ++k) {
+      const uint32_t kb = uint32_t(16 * 64 * NBL * (k >> 2));
+      const u32x2 a = *reinterpret_cast<const MHG_LDS u32x2 *>(size_t(rb + qo[k & 3] + kb));
+      const u32x2 b = *reinterpret_cast<const MHG_LDS u32x2 *>(size_t(rb2 + qo[k & 3] + kb));
+      const int soff = int((32 * (k >> 2) + 4 * (k & 3)) * p.ldc * 2);
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{a.x, a.y, b.x, b.y}, rs, voff, soff, kStoreDeviceScope);
     }
   }
 
