@@ -755,6 +755,11 @@ struct W8Gemm {
 #pragma unroll
           for (int j = 0; j < NBL; ++j) acc[i][j] = epilogue4pb(p, acc[i][j], f32x4{0.0f, 0.0f, 0.0f, 0.0f}, b[j], 4);
       }
+      if (p.out_code == E_F32 && !p.epi && rowW + 16 * NI <= p.M && colW + WTN <= p.N &&
+          (int64_t(16 * NI) * p.ldc + WTN) * 4 < (int64_t(1) << 31)) {
+        staged32_inside<I0, NI>(lane, region, rowW, colW);
+        return;
+      }
       if (p.out_code == E_F32 || (p.epi && p.beta != 0.0f)) {
         // Up to 64 rows (nb blocks) of 256 bytes a pass; chunk c of row r at
         // 16 (c ^ (r % 16)), which keeps the 16-byte writes (16 rows at 4 chunks) and the
@@ -928,6 +933,41 @@ struct W8Gemm {
       const u32x2 b = *reinterpret_cast<const MHG_LDS u32x2 *>(size_t(rb2 + qo[k & 3] + kb));
       const int soff = int((32 * (k >> 2) + 4 * (k & 3)) * p.ldc * 2);
       __builtin_amdgcn_raw_buffer_store_b128(u32x4{a.x, a.y, b.x, b.y}, rs, voff, soff, kStoreDeviceScope);
+    }
+  }
+
+  // The fp32 staged epilogue above, lean in the same way, for a wave block wholly inside
+  // C with no fused epilogue.  With t = lane % 16 and g = lane / 16, the write of block
+  // (i4, j) goes to row 16 i4 + t, chunk (4 j + g) ^ t = ((g ^ t) % 4) + 4 (j ^ (t / 4));
+  // read-back k takes row 4 k + g, chunk u ^ (4 (k % 4) + g) = ((u ^ g) % 4) + 4 (((u ^ g)
+  // / 4) ^ (k % 4)), u = lane % 16: four per-lane offsets each, the rest immediate.
+  template <int I0, int NI>
+  __device__ __forceinline__ void staged32_inside(int lane, uint32_t region, int64_t rowW, int64_t colW) {
+    const int t = lane & 15, g = lane >> 4, u = lane & 15, ug = u ^ g;
+    uint32_t woff[NBL], roff[4];
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) woff[j] = region + uint32_t(t * 256 + 16 * ((g ^ t) & 3) + 64 * (j ^ (t >> 2)));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) roff[q] = region + uint32_t(g * 256 + 16 * (ug & 3) + 64 * ((ug >> 2) ^ q));
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(static_cast<const char *>(p.C) + (rowW * p.ldc + colW) * 4);
+    const uint32_t voff = uint32_t((g * p.ldc + 4 * u) * 4);
+#pragma unroll
+    for (int pass = 0; pass < (NI + 3) / 4; ++pass) {
+      const int nb = NI - 4 * pass < 4 ? NI - 4 * pass : 4;
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+#pragma unroll
+        for (int j = 0; j < NBL; ++j) {
+          if (i4 >= nb) break;
+          *reinterpret_cast<MHG_LDS f32x4 *>(size_t(woff[j] + uint32_t(4096 * i4))) = acc[I0 + 4 * pass + i4][j];
+        }
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        if (k >= 4 * nb) break;
+        const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(roff[k & 3] + uint32_t(1024 * k)));
+        const int soff = int((64 * pass + 4 * k) * p.ldc * 4);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, soff, kStoreDeviceScope);
+      }
     }
   }
 

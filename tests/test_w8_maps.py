@@ -388,3 +388,35 @@ def test_plain_row_swizzle_would_conflict():
     addrs = [(l & 15) * 64 + 16 * ((l >> 4) ^ ((l & 15) >> 2 & 3)) for l in range(64)]
     assert all(_conflict_free(addrs[16 * g:16 * g + 16], 16) for g in range(4))
     assert not all(_conflict_free(g, 16) for g in _passes16(addrs))
+
+
+def test_lean_epilogue_offsets_match_the_general_maps():
+    """The lean epilogues (wave blocks inside C, no fused epilogue) split each staging
+    address into per-lane offsets computed once and immediate parts; they must land on
+    exactly the addresses of the general maps above."""
+    for lane in range(64):
+        t, g = lane & 15, lane >> 4
+        # fp32: writes of block (i4, j), read-back k
+        for j in range(4):
+            for i4 in range(4):
+                r, c = 16 * i4 + t, 4 * j + g
+                assert t * 256 + 16 * ((g ^ t) & 3) + 64 * (j ^ (t >> 2)) + 4096 * i4 == r * 256 + 16 * (c ^ swz16(r))
+        u = lane & 15
+        for k in range(16):
+            r = 4 * k + g
+            lean = g * 256 + 16 * ((u ^ g) & 3) + 64 * (((u ^ g) >> 2) ^ (k & 3)) + 1024 * k
+            assert lean == r * 256 + 16 * (u ^ swz16(r))
+        # 16-bit: writes of pair i2 in column block j, read-back k (row and both pieces)
+        for i2 in range(4):
+            for j in range(4):
+                woff = 16 * (64 * j + 16 * g + (t ^ (4 * j + 2 * (g >> 1) + (g & 1))))
+                assert woff + 16 * 64 * 4 * i2 == 16 * stage16_slot(i2, j, lane)
+        rho, c = lane >> 3, lane & 7
+        sh, r2, jj, cb = rho & 1, rho >> 1, c >> 1, c & 1
+        rb = 16 * (64 * jj + 32 * cb + (r2 ^ (2 * cb))) + 8 * sh
+        rb2 = 16 * (64 * jj + 32 * cb + 16 + (r2 ^ (2 * cb + 1))) + 8 * sh
+        for k in range(16):
+            qo, kb = 64 * ((k & 3) ^ jj), 4096 * (k >> 2)
+            row, col, (a0, a1) = stage16_read(k, lane)
+            assert (rb + qo + kb, rb2 + qo + kb) == (a0, a1)
+            assert (32 * (k >> 2) + 4 * (k & 3) + 16 * sh + r2, 8 * c) == (row, col)
