@@ -460,8 +460,10 @@ def summarize_trace(trace_csv, digest, out_path, settle, warmup, steps, workload
     for k in durs:
         durs[k].sort()
     rows = sorted(durs, key=lambda k: -sum(d for _, d in durs[k]))
+    # The headline line runs first: its kernel is the first GEMM kernel dispatched (the
+    # other lines settle for a fixed time, so a short kernel has more dispatches).
     head = [k for k in rows if "mhg::" in k and "gemm" in k]
-    hk = max(head, key=lambda k: len(durs[k]))
+    hk = min(head, key=lambda k: durs[k][0][0])
     timed = [d for _, d in durs[hk][settle + warmup:settle + warmup + steps]]
     lines = [
         "# Kernel durations of a default bench.py run (rocprofv3 kernel trace)",

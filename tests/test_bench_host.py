@@ -43,3 +43,23 @@ def test_traffic_only_for_the_matching_digest(tmp_path, monkeypatch):
     assert bench.traffic_for("w") is None
     assert bench.traffic_for("absent") is None
     assert not os.path.exists(prof / "counters_absent.txt")
+
+
+def test_trace_summary_takes_the_first_gemm_kernel_as_the_headline(tmp_path):
+    # A later, shorter kernel with more dispatches (a per-shape line that settles for a
+    # fixed time) must not be taken for the headline.
+    rows = ["Kernel_Name,Start_Timestamp,End_Timestamp"]
+    t = 1000
+    for i in range(6):                         # headline: 2 untimed + 3 timed + 1 more
+        rows.append(f'"void mhg::w8::w8_gemm<Big>(x)",{t},{t + 100 + i}')
+        t += 200
+    for i in range(20):
+        rows.append(f'"void mhg::w8::w8_gemm<Small>(x)",{t},{t + 8}')
+        t += 20
+    rows.insert(1, f'"elementwise_copy",{10},{20}')
+    csv_path, out = tmp_path / "kt.csv", tmp_path / "out.txt"
+    csv_path.write_text("\n".join(rows) + "\n")
+    bench.summarize_trace(str(csv_path), "d" * 16, str(out), 1, 1, 3, "w")
+    text = out.read_text()
+    assert "# Headline kernel (w): void mhg::w8::w8_gemm<Big>(x)" in text
+    assert "headline_timed_mean_ns: 103  (dispatches 3 .. 5 of it)" in text
