@@ -599,11 +599,19 @@ struct W8Gemm {
       // it.  Group 0 requests A of slab t+4 in phase 2t, group 1 B of slab t+4 in phase
       // 2t+1; slab t+1 must be in LDS when phase 2t+2 starts, so before every barrier
       // each wave waits until at most its three younger slabs' loads (12) are in flight.
-#pragma unroll
-      for (int t = 0; t < AHEAD; ++t) issue_all(t);
-      wait_vm<3 * LOADS>();             // slab 0 landed
+      // Prologue: slabs 0 and 1, then (once slab 0 has landed and the groups are one
+      // phase apart) slabs 2 and 3, first read four and six phases on.  Requests are
+      // throttled at issue when every wave of every compute unit makes them at once, so
+      // issuing all four first delayed the wait for slab 0 by the issue time of the
+      // other two.
+      issue_all(0);
+      issue_all(1);
+      wait_vm<LOADS>();                 // slab 0 landed
       barrier();
       if (grp == 1) barrier();
+      MHG_ORDER();
+      issue_all(2);
+      issue_all(3);
       MHG_ORDER();
       // The last four iterations would request the slabs past K.  With the prior C they
       // load it; otherwise they request nothing, and each waits for exactly the slabs
@@ -645,6 +653,9 @@ struct W8Gemm {
       // requested while slab t is multiplied.  Slab t + 2 must be in LDS when phase t + 2
       // starts, so after multiplying a wave waits until only its slab t + 4 (8 loads) is
       // in flight; slabs past K load zeros, so both groups run the same trip count.
+      // (Issuing the group's second slab only after its first had landed, as the
+      // 256 x 256 prologue does with slabs 2 and 3, was slower here: that slab is read
+      // two phases on and then arrived late; 1024^3 8.4-8.7 -> 8.7 us.)
       issue_all(int(grp));
       issue_all(int(grp) + 2);
       wait_vm<2 * LOADS>();             // the group's first slab landed
