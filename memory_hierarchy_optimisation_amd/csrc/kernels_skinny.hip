@@ -242,6 +242,10 @@ template <class H>
 __global__ void __launch_bounds__(NT, 2) skinny_gemm(LaunchArgs p) {
   __shared__ float red[4][16][BN];
   __shared__ int last;
+  // The arguments the stream needs, and those the compiler fetches early anyway, in
+  // scalar registers before anything else: requested together, waited for once.
+  asm volatile("" ::"s"(p.gn), "s"(p.split_k), "s"(p.A), "s"(p.B), "s"(p.M), "s"(p.N), "s"(p.K), "s"(p.lda),
+               "s"(p.ldb), "s"(p.epi), "s"(p.alpha), "s"(p.beta));
   Skinny<H> s(p);
   s.run(red, &last);
 }
