@@ -993,6 +993,12 @@ struct W8Gemm {
   }
   __device__ __forceinline__ void epilogue_prior(int lane) {
     const int64_t rowW = m0 + wm * WTM, colW = n0 + wn * WTN;
+    if (p.out_code == kHalfOut && rowW + WTM <= p.M && colW + WTN <= p.N &&
+        (int64_t(WTM) * p.ldc + WTN) * 2 < (int64_t(1) << 31)) {
+      if (p.act == 1) prior_inside<true>(lane, rowW, colW);
+      else prior_inside<false>(lane, rowW, colW);
+      return;
+    }
     f32x4 b[NBL];
 #pragma unroll
     for (int j = 0; j < NBL; ++j) {
@@ -1025,6 +1031,68 @@ struct W8Gemm {
       const int rr = 8 * k + (lane >> 3), cc = lane & 7;
       const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(prior_at(wm * WTM + rr, wn * (WTN / 8) + cc)));
       store_chunk(rowW + rr, colW + 8 * cc, v, 8, rowW, colW);
+    }
+  }
+
+  // The prior-C epilogue for a wave block wholly inside C, lean like the staged ones:
+  // the prior C has the output's (and input's) 16-bit type, beta is not zero (this
+  // kernel runs only then), the activation is a template parameter, and the per-element
+  // arithmetic is epilogue4pb's, in the same order.  With t = lane % 16, g = lane / 16,
+  // the piece (i, j) sits at prior_at(128 wm + 16 i + t, 8 wn + 2 j + g / 2) + 8 (g % 2):
+  // slot KT + 2 wm + i / 4, half (i / 2) % 2, row 16 (i % 2) + t, chunk c ^ pswz(t); store
+  // k reads row 8 k + r3 (r3 = lane / 8), chunk (8 wn + lane % 8) ^ (4 (k % 2) + r3 / 2 +
+  // 8 (r3 % 2)) of slot KT + 2 wm + k / 8, half (k / 4) % 2.
+  static __device__ __forceinline__ f32x4 unpack_half(u32x2 h) {
+    f32x4 c;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint16_t u = uint16_t(h[e >> 1] >> (16 * (e & 1)));
+      c[e] = std::is_same<H, HalfBF16>::value ? float(__builtin_bit_cast(__bf16, u)) : float(__builtin_bit_cast(_Float16, u));
+    }
+    return c;
+  }
+  template <bool RELU>
+  __device__ __forceinline__ void prior_inside(int lane, int64_t rowW, int64_t colW) {
+    const int KT = (kdim + BK - 1) / BK;
+    const int t = lane & 15, g = lane >> 4;
+    f32x4 b[NBL];
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) b[j] = bias4(p, colW + piece_col(j, lane), 4);
+    const float alpha = p.alpha, beta = p.beta;
+    const uint32_t sA = slot_addr(KT + 2 * wm), sB = slot_addr(KT + 2 * wm + 1);
+    uint32_t lo[NBL];
+#pragma unroll
+    for (int j = 0; j < NBL; ++j) lo[j] = uint32_t(t * 512 + 16 * ((8 * wn + 2 * j + (g >> 1)) ^ pswz(t)) + 8 * (g & 1));
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NBL; ++j) {
+        const uint32_t base = (i < 4 ? sA : sB) + uint32_t(((i >> 1) & 1) * OP_BYTES + (i & 1) * 16 * 512);
+        MHG_LDS u32x2 *at = reinterpret_cast<MHG_LDS u32x2 *>(size_t(base + lo[j]));
+        const f32x4 c = unpack_half(*at);
+        f32x4 f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float x = alpha * acc[i][j][e];
+          x += beta * c[e];
+          x += b[j][e];
+          if (RELU) x = x > 0.0f ? x : 0.0f;
+          f[e] = x;
+        }
+        *at = pack_half(f);
+        MHG_ORDER();     // one piece at a time: hoisting every read would spill
+      }
+    const int r3 = lane >> 3, cc = lane & 7;
+    uint32_t so[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) so[q] = uint32_t(r3 * 512 + 16 * ((8 * wn + cc) ^ (4 * q + (r3 >> 1) + 8 * (r3 & 1))));
+    const __amdgpu_buffer_rsrc_t rs = rsrc_of(static_cast<const char *>(p.C) + (rowW * p.ldc + colW) * 2);
+    const uint32_t voff = uint32_t((r3 * p.ldc + 8 * cc) * 2);
+#pragma unroll
+    for (int k = 0; k < WTM / 8; ++k) {
+      const uint32_t at = (k < 8 ? sA : sB) + uint32_t(((k >> 2) & 1) * OP_BYTES + 8 * (k & 3) * 512) + so[k & 1];
+      const u32x4 v = *reinterpret_cast<const MHG_LDS u32x4 *>(size_t(at));
+      __builtin_amdgcn_raw_buffer_store_b128(v, rs, voff, int(8 * k * p.ldc * 2), kStoreDeviceScope);
     }
   }
 
