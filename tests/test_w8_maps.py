@@ -420,3 +420,39 @@ def test_lean_epilogue_offsets_match_the_general_maps():
             row, col, (a0, a1) = stage16_read(k, lane)
             assert (rb + qo + kb, rb2 + qo + kb) == (a0, a1)
             assert (32 * (k >> 2) + 4 * (k & 3) + 16 * sh + r2, 8 * c) == (row, col)
+
+
+def test_lean_prior_epilogue_offsets_match_prior_at():
+    """The prior C of the 256 x 256 fused epilogue sits in the ring's slots past K:
+    quarter q of the tile (rows 64 q ..) in the slot of slab KT + q, its halves of 32
+    rows OP_BYTES apart, rows of 512 bytes with chunk c at c ^ pswz(row).  The lean form
+    splits each address into uniform, per-lane and immediate parts."""
+    SLOTS, SLOT, OP = 5, 32768, 16384
+
+    def pswz(r):
+        return ((r >> 1) & 7) | ((r & 1) << 3)
+
+    def slot_addr(s):
+        return (s % SLOTS) * SLOT
+
+    def prior_at(KT, R, c):
+        r = R & 31
+        return slot_addr(KT + R // 64) + ((R >> 5) & 1) * OP + r * 512 + 16 * (c ^ pswz(r))
+
+    for KT in (1, 2, 3, 7, 128):
+        for wm in range(2):
+            for wn in range(4):
+                sA, sB = slot_addr(KT + 2 * wm), slot_addr(KT + 2 * wm + 1)
+                for lane in range(64):
+                    t, g = lane & 15, lane >> 4
+                    lo = [t * 512 + 16 * ((8 * wn + 2 * j + (g >> 1)) ^ pswz(t)) + 8 * (g & 1) for j in range(4)]
+                    for i in range(8):
+                        for j in range(4):
+                            R, Cc = 128 * wm + 16 * i + t, 64 * wn + 16 * j + 4 * g
+                            lean = (sA if i < 4 else sB) + ((i >> 1) & 1) * OP + (i & 1) * 16 * 512 + lo[j]
+                            assert lean == prior_at(KT, R, Cc >> 3) + 8 * ((Cc >> 2) & 1)
+                    r3, cc = lane >> 3, lane & 7
+                    so = [r3 * 512 + 16 * ((8 * wn + cc) ^ (4 * q + (r3 >> 1) + 8 * (r3 & 1))) for q in range(2)]
+                    for k in range(16):
+                        lean = (sA if k < 8 else sB) + ((k >> 2) & 1) * OP + 8 * (k & 3) * 512 + so[k & 1]
+                        assert lean == prior_at(KT, 128 * wm + 8 * k + r3, 8 * wn + cc)
