@@ -430,13 +430,13 @@ def summarize_counters(name, digest, csvs, out_path):
         f"algorithmic_bytes_per_launch: {alg:.0f}",
         f"traffic_over_algorithmic: {traffic / alg:.3f}",
         "registers (compiler report of this build): " + " ".join(f"{k}={v}" for k, v in res.items()),
-        "# commands, each a run of its own, from /tmp with TMPDIR=/tmp (R = the repository root):",
+        "# commands, each a run of its own, from /tmp with TMPDIR=/tmp (R = the repository root, OUT = an output folder):",
     ]
     for tag, counters in COUNTER_PASSES.items():
-        lines.append(f"#   timeout -s KILL 300 rocprofv3 --pmc {counters} --output-format csv -d R/gpurun_out/pmc_{name}_{tag} "
+        lines.append(f"#   timeout -s KILL 300 rocprofv3 --pmc {counters} --output-format csv -d OUT/pmc_{name}_{tag} "
                      f"-o p -- {PROFILE_CMD.format(w=name).replace('bench.py', 'R/bench.py')}")
     lines.append(f"#   python3 bench.py --workload {name} --summarize-counters <digest> "
-                 + " ".join(f"gpurun_out/pmc_{name}_{t}/p_counter_collection.csv" for t in COUNTER_PASSES))
+                 + " ".join(f"OUT/pmc_{name}_{t}/p_counter_collection.csv" for t in COUNTER_PASSES))
     with open(out_path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     log("\n".join(lines))
@@ -468,10 +468,10 @@ def summarize_trace(trace_csv, digest, out_path, settle, warmup, steps, workload
     lines = [
         "# Kernel durations of a default bench.py run (rocprofv3 kernel trace)",
         f"# kernel_source_digest: {digest}",
-        "# command (from /tmp with TMPDIR=/tmp; R = the repository root):",
-        "#   timeout -s KILL 900 rocprofv3 --kernel-trace --stats --output-format csv -d R/gpurun_out/prof_kt -o kt "
+        "# command (from /tmp with TMPDIR=/tmp; R = the repository root, OUT = an output folder):",
+        "#   timeout -s KILL 900 rocprofv3 --kernel-trace --stats --output-format csv -d OUT/prof_kt -o kt "
         "-- python3 R/bench.py",
-        f"#   python3 bench.py --summarize-trace gpurun_out/prof_kt/kt_kernel_trace.csv {digest}",
+        f"#   python3 bench.py --summarize-trace OUT/prof_kt/kt_kernel_trace.csv {digest}",
         f"# Headline kernel ({workload}): {hk}",
         f"# Its dispatches in the order made: {settle} settling calls, {warmup} warm-up calls, {steps} timed calls "
         "(HIP events around the batch), then 300 calls in groups of 10 and 600 beside the clock probe; later "
