@@ -44,8 +44,8 @@ ROTATE_BYTES = 512 << 20       # working set of rotated operand copies, > 256 MB
 # instead of 105-115); these calls (~0.2 s) let it settle, so that the warm-up and the
 # timed steps see the steady state whatever --warmup the caller passes.
 SETTLE_CALLS = 2000
-# Spread of the call times: 30 groups of 10 consecutive calls.
-PER_CALL_GROUPS, PER_CALL_GROUP_SIZE = 30, 10
+# Spread of the call times: the timed calls in 30 groups of consecutive calls.
+PER_CALL_GROUPS = 30
 # Window of the clock probe: 2,000,000 ticks of the 100 MHz real-time counter (20 ms).
 CLOCK_TICKS = 2_000_000
 
@@ -112,11 +112,21 @@ def clock_during(run, first):
     return 100.0 * cycles / ticks
 
 
+def tidy(r):
+    """A line's figures for the JSON output: times in ms to the nanosecond (so that a
+    mean can be compared with its own percentiles), other figures to four decimals."""
+    return {k: (round(v, 6 if "_ms" in k or k.startswith("ms_") else 4) if isinstance(v, float) else v)
+            for k, v in r.items()}
+
+
 def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock=False, rotate=True,
-            settle_s=0.0):
+            settle_s=0.0, min_group_ms=0.0):
     """Time `steps` calls after `settle` + `warmup` untimed calls.  Returns a dict of
     figures.  settle_s: before those, untimed calls in chunks of 50 until that many
     seconds have passed (the clock's settling takes time, not a number of calls).
+    min_group_ms (with per_call): raise `steps` so that each group of timed calls takes
+    at least that long by the warm-up's mean, which keeps the events between groups
+    (~2.5 us each in the stream) below a few tenths of a percent of short calls.
     epilogue: run through the fused epilogue with alpha = beta = 1, a bias and ReLU (C is
     read as well as written; its bytes and the bias's count in the GB/s).  clock:
     afterwards, read the shader clock during a further run of calls."""
@@ -162,32 +172,35 @@ def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock
                     run(settled + i)
                 settled += 50
                 torch.cuda.synchronize()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record(stream)
         for i in range(settle + warmup):
             run(i)
+        w1.record(stream)
         torch.cuda.synchronize()
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        if per_call and min_group_ms > 0 and settle + warmup > 0:
+            per = w0.elapsed_time(w1) / (settle + warmup)
+            size = max(steps // PER_CALL_GROUPS, math.ceil(min_group_ms / per))
+            steps = max(steps, PER_CALL_GROUPS * size)
+        # The timed calls, with a HIP event at their start, after every group of calls
+        # and at their end: the mean is the whole span over `steps`, and with per_call the
+        # spread between calls is the groups' means (10 consecutive calls a group at the
+        # default 300), taken from the same calls, so the mean is their average.  An event
+        # pair around every single call would add its own gap to every call.
+        groups = min(PER_CALL_GROUPS, steps) if per_call else 1
+        bounds = [(g * steps) // groups for g in range(groups + 1)]
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
         t0 = time.perf_counter()
-        ev0.record(stream)
-        for i in range(steps):
-            run(i)
-        ev1.record(stream)
+        evs[0].record(stream)
+        for g in range(groups):
+            for i in range(bounds[g], bounds[g + 1]):
+                run(i)
+            evs[g + 1].record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        event_ms = ev0.elapsed_time(ev1) / steps
-        calls = []
-        if per_call:
-            # The spread between calls: HIP events around each of 30 groups of 10
-            # consecutive calls (an event pair around every single call would add its own
-            # gap to every call), each group's mean per call.
-            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(PER_CALL_GROUPS)]
-            for g, (a, b) in enumerate(evs):
-                a.record(stream)
-                for i in range(PER_CALL_GROUP_SIZE):
-                    run(g * PER_CALL_GROUP_SIZE + i)
-                b.record(stream)
-            torch.cuda.synchronize()
-            calls = sorted(a.elapsed_time(b) / PER_CALL_GROUP_SIZE for a, b in evs)
+        event_ms = evs[0].elapsed_time(evs[-1]) / steps
+        calls = sorted(evs[g].elapsed_time(evs[g + 1]) / (bounds[g + 1] - bounds[g])
+                       for g in range(groups)) if per_call else []
         clock_mhz = clock_during(run, steps) if clock else None
     finally:
         mh.gemm_destroy(plan)
@@ -474,7 +487,7 @@ def summarize_trace(trace_csv, digest, out_path, settle, warmup, steps, workload
         f"#   python3 bench.py --summarize-trace OUT/prof_kt/kt_kernel_trace.csv {digest}",
         f"# Headline kernel ({workload}): {hk}",
         f"# Its dispatches in the order made: {settle} settling calls, {warmup} warm-up calls, {steps} timed calls "
-        "(HIP events around the batch), then 300 calls in groups of 10 and 600 beside the clock probe; later "
+        "(HIP events at their start, after every tenth and at their end), then 600 beside the clock probe; later "
         "dispatches of it belong to the fused-epilogue line (other flags) or the autotune sweep.",
         f"headline_timed_mean_ns: {sum(timed) / max(len(timed), 1):.0f}  (dispatches {settle + warmup + 1} .. "
         f"{settle + warmup + steps} of it)",
@@ -619,8 +632,9 @@ def main():
             # Every line settles first, for as long as the headline's settling calls take:
             # the clock that the previous line left is not the one a steady stream of
             # these calls settles to (with 300 untimed calls alone, ~7 ms at 2048^3, the
-            # timed batch still ran slower than the per-call groups after it).
-            r = head if name == args.workload else measure(name, 300, 300, per_call=True, settle_s=0.2)
+            # timed calls still ran slower than the same calls a moment later).  Short
+            # calls are timed in more calls, so that each group spans 1 ms.
+            r = head if name == args.workload else measure(name, 300, 300, per_call=True, settle_s=0.2, min_group_ms=1.0)
             shapes.append(r)
             log(f"[bench] {name}: {r['kernel_tflops']:.1f} TFLOP/s, {r['kernel_gbps']:.0f} GB/s, "
                 f"{100 * r['frac_of_roofline']:.1f}% of the {r['bound']} roofline, tile {r['tile']}")
@@ -629,13 +643,13 @@ def main():
         # The same settling as the headline and the per-shape lines' fixed warm-up: the
         # clock settles again after the smaller per-shape lines.
         r = measure(args.workload, 300, 300, settle=SETTLE_CALLS, per_call=True, epilogue=True, clock=True)
-        extras["epilogue"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        extras["epilogue"] = tidy(r)
         log(f"[bench] {r['workload']} (alpha, beta = 1, bias, ReLU): {r['kernel_tflops']:.1f} TFLOP/s, "
             f"kernel {r['kernel_ms_event'] * 1000:.1f} us against {head['kernel_ms_event'] * 1000:.1f} us plain")
         # Context only: the same calls on one operand copy, which stays in the Infinity
         # Cache (the graded figure above streams its operands from HBM).
         r = measure(args.workload, 300, 300, settle=SETTLE_CALLS, per_call=True, rotate=False)
-        extras["warm"] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        extras["warm"] = tidy(r)
         log(f"[bench] {r['workload']}: {r['kernel_tflops']:.1f} TFLOP/s, kernel {r['kernel_ms_event'] * 1000:.1f} us")
         extras["autotune"] = autotune_report([n for n in PER_SHAPE if n != "f32_64"])
         extras["transpose"] = transpose_report()
@@ -667,11 +681,11 @@ def main():
         "clock_mhz": round(head["clock_mhz"], 1) if "clock_mhz" in head else None,
         "clock_note": "average shader clock over 20 ms of further headline calls (s_memtime over "
                       "s_memrealtime on a one-wave probe on a second stream)",
+        "kernel_ms_event": head["kernel_ms_event"],
         "kernel_ms_p10_p50_p90": head.get("kernel_ms_p10_p50_p90"),
         "settle_calls": args.settle,
         "kernel_source_digest": kernel_source_digest(),
-        "per_shape": [{k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
-                      for r in shapes],
+        "per_shape": [tidy(r) for r in shapes],
     }
     line.update(extras)
     print(json.dumps(line), flush=True)

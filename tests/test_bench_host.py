@@ -63,3 +63,14 @@ def test_trace_summary_takes_the_first_gemm_kernel_as_the_headline(tmp_path):
     text = out.read_text()
     assert "# Headline kernel (w): void mhg::w8::w8_gemm<Big>(x)" in text
     assert "headline_timed_mean_ns: 103  (dispatches 3 .. 5 of it)" in text
+
+
+def test_tidy_keeps_times_to_the_nanosecond():
+    # A mean printed to 0.1 us would fall outside percentiles printed in full.
+    r = bench.tidy({"kernel_ms_event": 0.00849951, "ms_per_step": 0.0041234567, "tflops": 255.123456,
+                    "kernel_ms_p10_p50_p90": [0.0084, 0.0085, 0.0086], "grid": 256})
+    assert r == {"kernel_ms_event": 0.0085, "ms_per_step": 0.004123, "tflops": 255.1235,
+                 "kernel_ms_p10_p50_p90": [0.0084, 0.0085, 0.0086], "grid": 256}
+    assert bench.tidy({"kernel_ms_event": 0.0084996})["kernel_ms_event"] == 0.0085
+    assert bench.tidy({"kernel_ms_event": 0.0085004})["kernel_ms_event"] == 0.0085
+    assert bench.tidy({"kernel_ms_event": 0.0084994})["kernel_ms_event"] == 0.008499
