@@ -112,6 +112,19 @@ def clock_during(run, first):
     return 100.0 * cycles / ticks
 
 
+def group_bounds(steps, groups):
+    """Call indices where each of `groups` consecutive groups of the `steps` timed calls
+    starts (and, last, where they end): sizes differ by at most one."""
+    return [(g * steps) // groups for g in range(groups + 1)]
+
+
+def steps_for_groups(steps, per_call_ms, min_group_ms):
+    """Timed calls for PER_CALL_GROUPS groups of at least `min_group_ms` each, at
+    `per_call_ms` a call, and never fewer than `steps`."""
+    size = max(steps // PER_CALL_GROUPS, math.ceil(min_group_ms / per_call_ms))
+    return max(steps, PER_CALL_GROUPS * size)
+
+
 def tidy(r):
     """A line's figures for the JSON output: times in ms to the nanosecond (so that a
     mean can be compared with its own percentiles), other figures to four decimals."""
@@ -179,16 +192,14 @@ def measure(name, steps, warmup, settle=0, per_call=False, epilogue=False, clock
         w1.record(stream)
         torch.cuda.synchronize()
         if per_call and min_group_ms > 0 and settle + warmup > 0:
-            per = w0.elapsed_time(w1) / (settle + warmup)
-            size = max(steps // PER_CALL_GROUPS, math.ceil(min_group_ms / per))
-            steps = max(steps, PER_CALL_GROUPS * size)
+            steps = steps_for_groups(steps, w0.elapsed_time(w1) / (settle + warmup), min_group_ms)
         # The timed calls, with a HIP event at their start, after every group of calls
         # and at their end: the mean is the whole span over `steps`, and with per_call the
         # spread between calls is the groups' means (10 consecutive calls a group at the
         # default 300), taken from the same calls, so the mean is their average.  An event
         # pair around every single call would add its own gap to every call.
         groups = min(PER_CALL_GROUPS, steps) if per_call else 1
-        bounds = [(g * steps) // groups for g in range(groups + 1)]
+        bounds = group_bounds(steps, groups)
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(groups + 1)]
         t0 = time.perf_counter()
         evs[0].record(stream)

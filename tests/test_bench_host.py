@@ -74,3 +74,21 @@ def test_tidy_keeps_times_to_the_nanosecond():
     assert bench.tidy({"kernel_ms_event": 0.0084996})["kernel_ms_event"] == 0.0085
     assert bench.tidy({"kernel_ms_event": 0.0085004})["kernel_ms_event"] == 0.0085
     assert bench.tidy({"kernel_ms_event": 0.0084994})["kernel_ms_event"] == 0.008499
+
+
+def test_group_bounds_cover_the_calls_in_order():
+    for steps, groups in [(300, 30), (3540, 30), (7, 7), (301, 30), (1, 1)]:
+        b = bench.group_bounds(steps, groups)
+        assert b[0] == 0 and b[-1] == steps and len(b) == groups + 1
+        sizes = [b[g + 1] - b[g] for g in range(groups)]
+        assert min(sizes) >= 1 and max(sizes) - min(sizes) <= 1
+    assert bench.group_bounds(300, 30) == list(range(0, 301, 10))
+
+
+def test_short_calls_get_groups_of_at_least_the_minimum_span():
+    # 8.5 us calls: 118 a group of 1 ms, 30 groups.
+    assert bench.steps_for_groups(300, 0.0085, 1.0) == 30 * 118
+    # 100 us calls already span 1 ms in groups of 10: the 300 steps stay.
+    assert bench.steps_for_groups(300, 0.1, 1.0) == 300
+    # never fewer calls than asked for
+    assert bench.steps_for_groups(900, 0.5, 1.0) == 900
